@@ -1,0 +1,10 @@
+"""CPU oracle of the RRAttention sparse-prefill path (test infrastructure).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product library never loads it.  See rr_oracle.c
+for the definitions each function follows.
+"""
+from .oracle import (  # noqa: F401
+    build, lib_path, pool_keys, stride_scores, block_scores, select, attention,
+    set_threads, get_threads, mask_from_list, list_from_mask,
+)
