@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the RRAttention sparse prefill on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--cpu-baseline on|off]
+
+One step = one pass of the whole path over the workload (rr_estimate ->
+rr_select -> rr_sparse_attn on one stream, the same kernels rr_prefill
+enqueues).  Inputs are generated on the host from the workload's seed,
+uploaded, and resident in HBM before timing starts.  W untimed steps, then K
+timed steps between two device synchronisations; HIP events on the launch
+stream split each step into estimate / select / attend.
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value          dense-equivalent TFLOP/s = 4 d Hq L(L+1)/2 / step time
+  ms_per_step    sparse prefill attention time per layer (ms)
+  roofline       block-sparse attention kernel: algorithmic FLOPs of the kept
+                 blocks per launch / its average launch time, vs bf16 MFMA peak
+  cpu_baseline   the fp64 oracle on this host's cores over a stated sample of
+                 the same workload, scaled to the full workload
+Default workload: llama8b-128k (32/8 heads, d=128, L=131072, B=128, S=8,
+tau=0.9), batch 1, one layer.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def kept_block_flops(counts, idx, L, B, d):
+    """Algorithmic FLOPs of attention over the kept blocks (2 matmuls, causal
+    pairs only on the diagonal block, short last block counted exactly)."""
+    import torch
+    Hq, nb = counts.shape
+    I = torch.arange(nb, device=counts.device)
+    rows = torch.clamp(L - I * B, max=B)                       # queries in block I
+    pos = torch.arange(nb, device=counts.device)
+    valid = pos[None, None, :] < counts[:, :, None]
+    J = torch.where(valid, idx, torch.full_like(idx, -1))
+    diag = (J == I[None, :, None]) & valid
+    off = valid & ~diag
+    n_off = off.sum(dim=(0, 2)).double()                       # per block-row I
+    n_diag = diag.sum(dim=(0, 2)).double()
+    r = rows.double()
+    pairs = n_off * r * B + n_diag * r * (r + 1) / 2
+    return float(4.0 * d * pairs.sum().item()), int(valid.sum().item()), int(diag.sum().item())
+
+
+def cpu_baseline(w, g, kept_pairs_all, dense_flops, budget_rows):
+    """Time the fp64 oracle on a sample of block-rows and scale to the workload."""
+    import oracle
+    nb, B, S, Hq = w.nb, w.B, w.S, w.Hq
+    step = max(1, nb // budget_rows)
+    Is = sorted(set(list(range(0, nb, step)) + [nb - 1]))
+    rows = [(h, I) for h in range(Hq) for I in Is]
+    threads = oracle.get_threads()
+    t0 = time.perf_counter()
+    oracle.pool_keys(g["k"], S)
+    t_pool = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    A = oracle.block_scores(g["q"], g["k"], B, S, rows=rows)
+    t_est = time.perf_counter() - t0 - t_pool
+    I_of_row = np.array([I for _, I in rows], dtype=np.int32)
+    t0 = time.perf_counter()
+    keep, cnt, _ = oracle.select(A, w.tau, I_of_row=I_of_row)
+    t_sel = time.perf_counter() - t0
+    mask = np.zeros((Hq, nb, nb), dtype=np.uint8)
+    for r, (h, I) in enumerate(rows):
+        mask[h, I] = keep[r]
+    toks = []
+    for h, I in rows:
+        lo, hi = I * B, min(w.L, (I + 1) * B) - 1
+        for t in np.linspace(lo, hi, 4).astype(int):
+            toks.append((h, int(t)))
+    t0 = time.perf_counter()
+    oracle.attention(g["q"], g["k"], g["v"], B, mask, toks=toks)
+    t_att = time.perf_counter() - t0
+    # Work shares of the sample.
+    est_all = float(Hq) * sum((I + 1) for I in range(nb))
+    est_smp = float(sum(I + 1 for _, I in rows))
+    pairs_smp = 0.0
+    for h, t in toks:
+        I = t // B
+        pairs_smp += sum(min(B, t + 1 - J * B) for J in np.nonzero(mask[h, I])[0])
+    pairs_all = kept_pairs_all
+    T = (t_pool + t_est * est_all / est_smp + t_sel * est_all / est_smp
+         + t_att * pairs_all / max(1.0, pairs_smp))
+    sample = ("oracle E1 on all keys; E2-E5 on %d block-rows (every %d-th row of every head, plus "
+              "the last) = %.2f%% of the estimation work; E6 on %d tokens (4 per sampled block-row) "
+              "= %.4f%% of the attended (query, key) pairs; stage times scaled by those shares: pool %.2fs, "
+              "estimate %.2fs, select %.2fs, attend %.2fs measured"
+              % (len(rows), step, 100 * est_smp / est_all, len(toks),
+                 100 * pairs_smp / pairs_all, t_pool, t_est, t_sel, t_att))
+    return dict(value=dense_flops / T / 1e12, unit="TFLOP/s (dense-equivalent)", cores=threads,
+                kind="oracle", sample=sample, seconds_full_workload=T)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload index 0..4")
+    ap.add_argument("--S", type=int, default=None)
+    ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--cpu-rows", type=int, default=16, help="sampled block-rows per head")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path shards by whole kv-head groups with no "
+              "exchange, and this build runs on a single MI355X; --gpus %d is not supported"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_prefill_rr_amd as rr
+    from rr_workloads import generate, get_config
+
+    w = get_config(args.config)
+    if args.S is not None:
+        w = w.with_params(S=args.S)
+    if args.tau is not None:
+        w = w.with_params(tau=args.tau)
+    log("workload %s L=%d Hq=%d Hkv=%d d=%d B=%d S=%d tau=%g" % (w.name, w.L, w.Hq, w.Hkv, w.d,
+                                                                  w.B, w.S, w.tau))
+    t0 = time.perf_counter()
+    g = generate(w)
+    log("inputs generated in %.1fs" % (time.perf_counter() - t0))
+
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = up(g["q"]), up(g["k"]), up(g["v"])
+    L, Hq, Hkv, d, B, S, tau = w.L, w.Hq, w.Hkv, w.d, w.B, w.S, w.tau
+    nb = w.nb
+    A = torch.empty((Hq, nb, nb), dtype=torch.float32, device=dev)
+    counts = torch.empty((Hq, nb), dtype=torch.int32, device=dev)
+    idx = torch.empty((Hq, nb, nb), dtype=torch.int32, device=dev)
+    O = torch.empty((L, Hq, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(rr.prefill_workspace_bytes(L, Hq, Hkv, d, B, S), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log("resident in HBM: q %.0f MiB, k/v %.0f MiB each, workspace %.0f MiB"
+        % (q.numel() * 2 / 2**20, k.numel() * 2 / 2**20, ws.numel() / 2**20))
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        rr.rr_estimate(q, k, B, S, block_scores=A, ws=ws)
+        if evs is not None:
+            evs[1].record()
+        rr.rr_select(A, L, B, tau, counts=counts, block_idx=idx)
+        if evs is not None:
+            evs[2].record()
+        rr.rr_sparse_attn(q, k, v, B, counts, idx, out=O, ws=ws)
+        if evs is not None:
+            evs[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done (%d steps)" % args.warmup)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    est = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    sel = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    att = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    tot = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    ms = float(tot.mean())
+    log("timed %d steps: %.3f ms/step (events), %.3f ms/step (wall)" % (args.steps, ms,
+                                                                        1e3 * wall / args.steps))
+
+    # rr_prefill, the single-call form of the same step.
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    pe[0].record()
+    for _ in range(args.steps):
+        rr.rr_prefill(q, k, v, B, S, tau, out=O, counts=counts, block_idx=idx, ws=ws)
+    pe[1].record()
+    torch.cuda.synchronize()
+    prefill_ms = pe[0].elapsed_time(pe[1]) / args.steps
+
+    flops_kept, n_kept, n_diag = kept_block_flops(counts, idx, L, B, d)
+    dense_flops = 4.0 * d * Hq * L * (L + 1) / 2.0
+    causal_blocks = Hq * nb * (nb + 1) // 2
+    att_ms = float(att.mean())
+    achieved = flops_kept / (att_ms * 1e-3) / 1e12
+    alg_bytes_est = (L * Hkv * d * 2 + (L // S) * Hq * d * 2 + Hq * nb * (nb + 1) // 2 * 4 * 2
+                     + Hq * nb * 4 + Hq * nb * (nb + 1) // 2 * 4)
+    score_ms = float(est.mean() + sel.mean())
+    out = {
+        "metric": "sparse prefill attn ms/layer + dense-equiv TFLOP/s at 128K; scoring GB/s",
+        "value": dense_flops / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded generator of the workload's shape; no dataset, no weights)",
+        "config": {"workload": w.name, "batch": 1, "L": L, "Hq": Hq, "Hkv": Hkv, "d": d, "B": B,
+                   "S": S, "tau": tau, "layers": 1, "parallelism": "none (1 GPU)"},
+        "stages_ms": {"estimate": float(est.mean()), "select": float(sel.mean()),
+                      "attend": att_ms, "prefill_single_call": prefill_ms,
+                      "wall_per_step": 1e3 * wall / args.steps},
+        "density": n_kept / causal_blocks,
+        "kept_blocks": n_kept,
+        "kept_diagonal_blocks": n_diag,
+        "scoring": {"ms": score_ms, "algorithmic_bytes": alg_bytes_est,
+                    "GBps_algorithmic": alg_bytes_est / (score_ms * 1e-3) / 1e9},
+        "roofline": {"kernel": "rr_block_sparse_fa (with its V transpose)", "bound": "mfma",
+                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "flops_per_launch": flops_kept},
+    }
+    if args.cpu_baseline == "on":
+        log("cpu baseline (oracle) on a sample ...")
+        t0 = time.perf_counter()
+        out["cpu_baseline"] = cpu_baseline(w, g, flops_kept / (4.0 * d), dense_flops,
+                                           args.cpu_rows)
+        log("cpu baseline done in %.1fs" % (time.perf_counter() - t0))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

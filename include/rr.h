@@ -1,0 +1,131 @@
+/*
+ * rr.h -- C ABI of the RRAttention sparse-prefill library (librr.so, gfx950).
+ *
+ * The method (RRAttention, arXiv 2602.05853): a per-head round-robin sample of
+ * one query per stride of S tokens is scored against stride-pooled keys, a
+ * causal stride-level softmax is pooled into B x B block scores, an adaptive
+ * Top-tau rule keeps the smallest set of key blocks per query block-row whose
+ * probability mass reaches tau, and causal attention runs on the kept blocks
+ * only (RRAttention summary page, "Summary" and "Key points"; abstract; the
+ * Top-tau rule follows the find_blocks definition on the XAttention review
+ * page, "threshold block selection").
+ *
+ * Conventions for every entry point
+ *  - Tensor pointers are DEVICE pointers to contiguous memory, batch 1.
+ *    Q and O are [L][Hq][d]; K and V are [L][Hkv][d]; bf16 travels as its
+ *    16-bit pattern (uint16_t).  Query head h reads kv-head h / (Hq/Hkv).
+ *  - nb = ceil(L / B) key/query blocks; ns = L / S strides.
+ *  - Supported shapes: d in {64, 128}; B in {64, 128}; S a power of two with
+ *    S <= B; L % S == 0 (L % B may be nonzero: the last block is short);
+ *    Hq % Hkv == 0; nb <= 4096.
+ *  - The caller owns every buffer (inputs, outputs and workspace).  The
+ *    library never allocates, frees or synchronises; all work is enqueued on
+ *    `stream` (a hipStream_t passed as void*, NULL = the null stream) and the
+ *    call returns as soon as it is enqueued.  Nothing outside the given
+ *    buffers is written.  Results are ready when the stream reaches them.
+ *  - Errors: argument checks run on the host before any launch and return a
+ *    nonzero rr_status with no work enqueued; RR_E_HIP reports a failed
+ *    launch (outputs are then undefined).  The library keeps no state and
+ *    may be called from several host threads at once (on distinct buffers).
+ */
+#ifndef RR_H
+#define RR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RR_OK = 0,
+    RR_E_NULL = 1,        /* a required pointer is NULL */
+    RR_E_SHAPE = 2,       /* non-positive size, Hq % Hkv, B % S or L % S nonzero, S > B */
+    RR_E_TAU = 3,         /* tau is NaN or outside (0, 1] */
+    RR_E_WORKSPACE = 4,   /* ws_bytes below the required workspace size */
+    RR_E_UNSUPPORTED = 5, /* d, B or S outside the compiled instantiations, nb too large */
+    RR_E_HIP = 6          /* a HIP launch failed */
+} rr_status;
+
+typedef enum {
+    RR_OUT_BF16 = 0, /* O stored as bf16 (round to nearest even from fp32) */
+    RR_OUT_F32 = 1   /* O stored as fp32 */
+} rr_out_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *rr_status_str(int status);
+
+/* ABI version of this header (incremented on incompatible change). */
+int rr_abi_version(void);
+
+/*
+ * Workspace sizes in bytes (0 if the shape is invalid).  The prefill size is
+ * large enough for each of the three stage calls as well.
+ */
+size_t rr_estimate_workspace_bytes(int L, int Hq, int Hkv, int d, int B, int S);
+size_t rr_sparse_attn_workspace_bytes(int L, int Hq, int Hkv, int d, int B);
+size_t rr_prefill_workspace_bytes(int L, int Hq, int Hkv, int d, int B, int S);
+
+/*
+ * rr_estimate -- block scores of the round-robin estimate.
+ * Per stride j and kv-head g the pooled key is the mean of the stride's S
+ * keys ("scores are pooled per stride", RRAttention summary page, Summary).
+ * Query head h scores token i*S + (h mod S) of every stride i (the offset
+ * rotates from head to head, same passage) against pooled keys j <= i with
+ * scale 1/sqrt(d); each such row is normalised by a softmax over j <= i
+ * (stride-level softmax, Key points), and the probabilities are summed over
+ * B x B blocks (stride-level aggregation, abstract).
+ *   block_scores  out, fp32 [Hq][nb][nb]; entry (h, I, J) for J <= I, zero
+ *                 for J > I.  Block-row I sums to the number of strides in
+ *                 block I (B/S, fewer for a short last block).
+ *   ws, ws_bytes  device workspace, >= rr_estimate_workspace_bytes(...).
+ */
+int rr_estimate(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv, int d, int B,
+                int S, float *block_scores, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * rr_select -- adaptive Top-tau per (query head, query block-row).
+ * For block-row I of head h with W = sum_{J<=I} A[h][I][J]: order the blocks
+ * by (score descending, block index ascending) and keep the shortest prefix
+ * whose cumulative score is >= tau * W (find_blocks, XAttention review page,
+ * threshold block selection); tau = 1 keeps every causal block.  Sums run in
+ * fp32.
+ *   block_scores  in, fp32 [Hq][nb][nb] (as written by rr_estimate).
+ *   counts        out, int32 [Hq][nb]: number of kept blocks (>= 1).
+ *   block_idx     out, int32 [Hq][nb][nb]: kept key-block indices of row
+ *                 (h, I) in ascending order in its first counts[h][I]
+ *                 entries, -1 in the rest.
+ */
+int rr_select(const float *block_scores, int Hq, int L, int B, float tau, int32_t *counts,
+              int32_t *block_idx, void *stream);
+
+/*
+ * rr_sparse_attn -- causal block-sparse attention with GQA over a compacted
+ * block list (attention computed only on the kept blocks, abstract).
+ * For token t in block I = t / B and head h the keys are the n <= t whose
+ * block n / B is listed in block_idx[h][I][0 .. counts[h][I]); softmax of
+ * (1/sqrt(d)) Q[t][h] . K[n][g] over them, applied to V[n][g].
+ * Lists must be ascending, in range J <= I, and non-empty.
+ *   O         out, [L][Hq][d] in o_dtype (rr_out_dtype).
+ *   ws        device workspace, >= rr_sparse_attn_workspace_bytes(...).
+ */
+int rr_sparse_attn(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, int Hq,
+                   int Hkv, int d, int B, const int32_t *counts, const int32_t *block_idx,
+                   void *O, int o_dtype, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * rr_prefill -- the whole path: rr_estimate, rr_select and rr_sparse_attn on
+ * one stream, with the block scores kept in the workspace.
+ *   counts, block_idx  out, as for rr_select (the mask that was applied).
+ *   ws                 device workspace, >= rr_prefill_workspace_bytes(...).
+ */
+int rr_prefill(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, int Hq, int Hkv,
+               int d, int B, int S, float tau, void *O, int o_dtype, int32_t *counts,
+               int32_t *block_idx, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RR_H */

@@ -1,0 +1,12 @@
+"""MI355X-native RRAttention sparse prefill.
+
+The compute lives in librr.so (hand-written HIP kernels for gfx950 behind the
+C ABI of include/rr.h); :mod:`long_context_prefill_rr_amd.rr` marshals torch
+tensors into those calls.  Importing the binding fails loudly when librr.so
+is missing: there is no fallback path.
+"""
+from .rr import (  # noqa: F401
+    RRError, lib_path, load_library, rr_estimate, rr_select, rr_sparse_attn, rr_prefill,
+    estimate_workspace_bytes, sparse_attn_workspace_bytes, prefill_workspace_bytes,
+    RR_OUT_BF16, RR_OUT_F32,
+)

@@ -1,0 +1,154 @@
+// rr_api.hip -- the C ABI of librr (declared in include/rr.h).
+//
+// Host-side argument checks, workspace carving and the launch sequence of
+// each stage.  No allocation, no synchronisation: every kernel is enqueued on
+// the caller's stream.
+#include <math.h>
+
+#include "rr.h"
+#include "rr_internal.h"
+
+using namespace rr;
+
+namespace {
+
+constexpr int kMaxBlocks = 4096;  // longest Top-tau row the selection kernel sorts
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int check_shape(int L, int Hq, int Hkv, int d, int B, int S, bool need_S) {
+    if (L <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || B <= 0) return RR_E_SHAPE;
+    if (Hq % Hkv != 0) return RR_E_SHAPE;
+    if (need_S) {
+        if (S <= 0 || S > B || B % S != 0 || L % S != 0) return RR_E_SHAPE;
+        if (!is_pow2(S)) return RR_E_UNSUPPORTED;
+    }
+    if (d != 64 && d != 128) return RR_E_UNSUPPORTED;
+    if (B != 64 && B != 128) return RR_E_UNSUPPORTED;
+    if ((L + B - 1) / B > kMaxBlocks) return RR_E_UNSUPPORTED;
+    // Element offsets are formed in 64-bit; the largest tensor must still fit
+    // the 32-bit grid decode of the kernels.
+    if ((long long)L * Hq > (1ll << 40)) return RR_E_UNSUPPORTED;
+    return RR_OK;
+}
+
+int check_tau(float tau) {
+    if (isnan(tau) || !(tau > 0.f) || tau > 1.f) return RR_E_TAU;
+    return RR_OK;
+}
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+int run_estimate(const uint16_t *Q, const uint16_t *K, const Shape &s, float *A, void *ws,
+                 hipStream_t st) {
+    EstimateWs w = carve_estimate(s, ws);
+    if (launch_pool_k(K, s, w.kplanes, st) != hipSuccess) return RR_E_HIP;
+    if (launch_score(Q, s, w, st) != hipSuccess) return RR_E_HIP;
+    if (launch_softmax_pool(s, w, A, st) != hipSuccess) return RR_E_HIP;
+    return RR_OK;
+}
+
+int run_attn(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const Shape &s,
+             const int32_t *counts, const int32_t *block_idx, void *O, int o_dtype, void *ws,
+             hipStream_t st) {
+    uint16_t *Vt = (uint16_t *)ws;
+    if (launch_transpose_v(V, s, Vt, st) != hipSuccess) return RR_E_HIP;
+    if (launch_block_sparse_fa(Q, K, Vt, s, counts, block_idx, O, o_dtype == RR_OUT_F32, st) !=
+        hipSuccess)
+        return RR_E_HIP;
+    return RR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rr_status_str(int status) {
+    switch (status) {
+        case RR_OK: return "RR_OK";
+        case RR_E_NULL: return "RR_E_NULL: a required pointer is NULL";
+        case RR_E_SHAPE: return "RR_E_SHAPE: invalid sizes (L, heads, d, B, S)";
+        case RR_E_TAU: return "RR_E_TAU: tau must lie in (0, 1]";
+        case RR_E_WORKSPACE: return "RR_E_WORKSPACE: workspace too small";
+        case RR_E_UNSUPPORTED: return "RR_E_UNSUPPORTED: d, B or S not compiled, or too many blocks";
+        case RR_E_HIP: return "RR_E_HIP: a HIP launch failed";
+        default: return "RR_E_UNKNOWN";
+    }
+}
+
+int rr_abi_version(void) { return 1; }
+
+size_t rr_estimate_workspace_bytes(int L, int Hq, int Hkv, int d, int B, int S) {
+    if (check_shape(L, Hq, Hkv, d, B, S, true) != RR_OK) return 0;
+    return estimate_ws_bytes(make_shape(L, Hq, Hkv, d, B, S));
+}
+
+size_t rr_sparse_attn_workspace_bytes(int L, int Hq, int Hkv, int d, int B) {
+    if (check_shape(L, Hq, Hkv, d, B, 1, false) != RR_OK) return 0;
+    return attn_ws_bytes(make_shape(L, Hq, Hkv, d, B, 1));
+}
+
+size_t rr_prefill_workspace_bytes(int L, int Hq, int Hkv, int d, int B, int S) {
+    if (check_shape(L, Hq, Hkv, d, B, S, true) != RR_OK) return 0;
+    const Shape s = make_shape(L, Hq, Hkv, d, B, S);
+    const size_t a = align_up((size_t)s.Hq * s.nb * s.nb * 4);
+    const size_t e = estimate_ws_bytes(s), t = attn_ws_bytes(s);
+    return a + (e > t ? e : t);
+}
+
+int rr_estimate(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv, int d, int B, int S,
+                float *block_scores, void *ws, size_t ws_bytes, void *stream) {
+    if (!Q || !K || !block_scores || !ws) return RR_E_NULL;
+    int rc = check_shape(L, Hq, Hkv, d, B, S, true);
+    if (rc != RR_OK) return rc;
+    const Shape s = make_shape(L, Hq, Hkv, d, B, S);
+    if (ws_bytes < estimate_ws_bytes(s)) return RR_E_WORKSPACE;
+    return run_estimate(Q, K, s, block_scores, ws, as_stream(stream));
+}
+
+int rr_select(const float *block_scores, int Hq, int L, int B, float tau, int32_t *counts,
+              int32_t *block_idx, void *stream) {
+    if (!block_scores || !counts || !block_idx) return RR_E_NULL;
+    if (L <= 0 || Hq <= 0 || B <= 0) return RR_E_SHAPE;
+    if ((L + B - 1) / B > kMaxBlocks) return RR_E_UNSUPPORTED;
+    int rc = check_tau(tau);
+    if (rc != RR_OK) return rc;
+    const Shape s = make_shape(L, Hq, Hq, 64, B, 1);
+    if (launch_topk_tau(block_scores, s, tau, counts, block_idx, as_stream(stream)) != hipSuccess)
+        return RR_E_HIP;
+    return RR_OK;
+}
+
+int rr_sparse_attn(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, int Hq, int Hkv,
+                   int d, int B, const int32_t *counts, const int32_t *block_idx, void *O,
+                   int o_dtype, void *ws, size_t ws_bytes, void *stream) {
+    if (!Q || !K || !V || !counts || !block_idx || !O || !ws) return RR_E_NULL;
+    int rc = check_shape(L, Hq, Hkv, d, B, 1, false);
+    if (rc != RR_OK) return rc;
+    if (o_dtype != RR_OUT_BF16 && o_dtype != RR_OUT_F32) return RR_E_UNSUPPORTED;
+    const Shape s = make_shape(L, Hq, Hkv, d, B, 1);
+    if (ws_bytes < attn_ws_bytes(s)) return RR_E_WORKSPACE;
+    return run_attn(Q, K, V, s, counts, block_idx, O, o_dtype, ws, as_stream(stream));
+}
+
+int rr_prefill(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, int Hq, int Hkv,
+               int d, int B, int S, float tau, void *O, int o_dtype, int32_t *counts,
+               int32_t *block_idx, void *ws, size_t ws_bytes, void *stream) {
+    if (!Q || !K || !V || !O || !counts || !block_idx || !ws) return RR_E_NULL;
+    int rc = check_shape(L, Hq, Hkv, d, B, S, true);
+    if (rc != RR_OK) return rc;
+    rc = check_tau(tau);
+    if (rc != RR_OK) return rc;
+    if (o_dtype != RR_OUT_BF16 && o_dtype != RR_OUT_F32) return RR_E_UNSUPPORTED;
+    const Shape s = make_shape(L, Hq, Hkv, d, B, S);
+    if (ws_bytes < rr_prefill_workspace_bytes(L, Hq, Hkv, d, B, S)) return RR_E_WORKSPACE;
+    hipStream_t st = as_stream(stream);
+    float *A = (float *)ws;
+    void *rest = (char *)ws + align_up((size_t)s.Hq * s.nb * s.nb * 4);
+    rc = run_estimate(Q, K, s, A, rest, st);
+    if (rc != RR_OK) return rc;
+    if (launch_topk_tau(A, s, tau, counts, block_idx, st) != hipSuccess) return RR_E_HIP;
+    return run_attn(Q, K, V, s, counts, block_idx, O, o_dtype, rest, st);
+}
+
+}  // extern "C"

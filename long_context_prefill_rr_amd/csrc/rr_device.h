@@ -1,0 +1,61 @@
+// rr_device.h -- device-side helpers shared by the librr kernels (gfx950).
+//
+// Vector types for the CDNA4 bf16 matrix instructions, 16-byte global/LDS
+// accesses, bf16 rounding and wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rr {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
+
+__device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void st16(uint16_t *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+
+__device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// fp32 -> bf16 bit pattern, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    __bf16 b = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Two fp32 -> packed bf16x2 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return (uint32_t)bf16_bits(a) | ((uint32_t)bf16_bits(b) << 16);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of lane (lane ^ m) in a 64-wide wave.
+__device__ __forceinline__ float xor_lane(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+// Merge two (max, sum-of-2^(x-max)) pairs.  (-inf, 0) is the identity.
+__device__ __forceinline__ void merge_max_sum(float &m, float &z, float m2, float z2) {
+    float nm = fmaxf(m, m2);
+    if (nm == -INFINITY) return;
+    z = z * fast_exp2(m - nm) + z2 * fast_exp2(m2 - nm);
+    m = nm;
+}
+
+}  // namespace rr

@@ -1,0 +1,359 @@
+// rr_estimate.hip -- the estimation kernels of the round-robin block scores.
+//
+//   rr_pool_k               K -> stride-mean keys, split into three bf16 planes
+//   rr_score                sampled queries x pooled keys on bf16 MFMA; per
+//                           (row, key-block) running max / sum-of-exponentials
+//   rr_stride_softmax_pool  causal row softmax folded into B x B block sums
+//
+// Method: one query per stride of S tokens, offset h mod S rotating with the
+// query head, scored against the mean key of every earlier-or-equal stride,
+// softmax over strides, probabilities summed per block (RRAttention summary
+// page, "Summary" and "Key points"; RRAttention abstract).
+//
+// Precision: the pooled key is an fp32 mean of bf16 keys.  Rounding it to one
+// bf16 moves scores enough to flip Top-tau decisions, so it is carried as
+// hi + mid + lo bf16 planes (24 significand bits) and each plane is a
+// separate MFMA pass with fp32 accumulation.  Scores live in the log2 domain
+// (scaled by log2(e)/sqrt(d)) so exponentials are single v_exp_f32.
+#include "rr_device.h"
+#include "rr_internal.h"
+
+namespace rr {
+
+// ---------------------------------------------------------------------------
+// rr_pool_k: Kbar[g][j][:] = (1/S) sum_t K[jS+t][g][:], written as three bf16
+// planes.  One thread per (stride, kv-head, 8 consecutive channels); the
+// token-major K makes each group of d/8 threads read one contiguous key row.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void rr_pool_k(const uint16_t *__restrict__ K, int Hkv, int ns,
+                                                 int S, float invS,
+                                                 uint16_t *__restrict__ planes) {
+    constexpr int C8 = D / 8;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long total = (long long)ns * Hkv * C8;
+    if (idx >= total) return;
+    const int c8 = (int)(idx % C8);
+    const long long r = idx / C8;
+    const int g = (int)(r % Hkv);
+    const int j = (int)(r / Hkv);
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    const uint16_t *src = K + ((size_t)j * S * Hkv + g) * D + c8 * 8;
+    for (int t = 0; t < S; ++t) {
+        uint4 v = ld16(src + (size_t)t * Hkv * D);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += __uint_as_float(w[e] << 16);
+            acc[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+        }
+    }
+    uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float x0 = acc[2 * e] * invS, x1 = acc[2 * e + 1] * invS;
+        uint16_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
+        float r0 = x0 - bf16_to_f32(h0), r1 = x1 - bf16_to_f32(h1);
+        uint16_t m0 = bf16_bits(r0), m1 = bf16_bits(r1);
+        float q0 = r0 - bf16_to_f32(m0), q1 = r1 - bf16_to_f32(m1);
+        hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        mid[e] = (uint32_t)m0 | ((uint32_t)m1 << 16);
+        lo[e] = pack_bf16x2(q0, q1);
+    }
+    const size_t plane = (size_t)Hkv * ns * D;
+    uint16_t *dst = planes + ((size_t)g * ns + j) * D + c8 * 8;
+    st16(dst, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+    st16(dst + plane, make_uint4(mid[0], mid[1], mid[2], mid[3]));
+    st16(dst + 2 * plane, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+}
+
+// Offset of stride row i = I*C + a inside one head's packed (row, block) area.
+__device__ __forceinline__ long long packed_row_offset(int C, int I, int a) {
+    return (long long)C * I * (I + 1) / 2 + (long long)a * (I + 1);
+}
+
+// ---------------------------------------------------------------------------
+// rr_score: one work-group per (query block-row I, kv-head g, chunk of 64
+// sampled rows).  The rows are the (query head, stride) pairs of the G heads
+// that share kv-head g, for the C strides of block I: row (hh, a) samples
+// token (I*C + a)*S + ((g*G + hh) mod S).  Four waves split the key strides
+// 0 .. (I+1)*C-1 into groups of max(C, 16) and each wave computes, for all 64
+// rows, S^T = Kbar . Q^T tiles of 16 strides x 16 rows on
+// v_mfma_f32_16x16x32_bf16 (3 planes x d/32 steps).  For every (row,
+// key-block) it keeps max and sum of 2^(s - max) over the block's strides
+// j <= i and writes them; per-row totals are merged across waves into
+// rowstat.  Nothing of the [rows x strides] score matrix reaches memory.
+// ---------------------------------------------------------------------------
+template <int D, int C>
+__global__ __launch_bounds__(256) void rr_score(const uint16_t *__restrict__ Q,
+                                                const uint16_t *__restrict__ Kp, int Hq, int Hkv,
+                                                int S, int nb, int ns, int G, int nchunks,
+                                                long long P, float scale2,
+                                                float2 *__restrict__ stats,
+                                                float2 *__restrict__ rowstat) {
+    constexpr int KS = D / 32;
+    constexpr int KG = C >= 16 ? C : 16;
+    constexpr int NSUB = KG / 16;
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lr = lane & 15, lg = lane >> 4;
+
+    int b = blockIdx.x;
+    const int chunk = b % nchunks;
+    b /= nchunks;
+    const int g = b % Hkv;
+    const int I = nb - 1 - b / Hkv;
+    const int cI = min(C, ns - I * C);
+    const size_t plane = (size_t)Hkv * ns * D;
+    const uint16_t *kb = Kp + (size_t)g * ns * D;
+    const int rows_here = min(64, G * C - chunk * 64);
+    const int NT = (rows_here + 15) >> 4;
+
+    bf16x8 qf[4][KS];
+    int row_i[4], row_h[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const int f = chunk * 64 + rt * 16 + lr;
+        const int hh = f / C, a = f % C;
+        const bool valid = (rt < NT) && hh < G && a < cI;
+        row_i[rt] = valid ? I * C + a : -1;
+        row_h[rt] = g * G + (hh < G ? hh : 0);
+        const int t = valid ? row_i[rt] * S + (row_h[rt] % S) : 0;
+        const uint16_t *qp = Q + ((size_t)t * Hq + row_h[rt]) * D + lg * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[rt][ks] = valid ? as_bf16x8(ld16(qp + ks * 32)) : as_bf16x8(zero_u4());
+    }
+
+    float rM[4], rZ[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        rM[rt] = -INFINITY;
+        rZ[rt] = 0.f;
+    }
+
+    const int nkeys = (I + 1) * C;
+    const int ngroups = (nkeys + KG - 1) / KG;
+    for (int u = wid; u < ngroups; u += 4) {
+        if constexpr (C >= 16) {
+            const int J = u;
+            float bm[4], bz[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                bm[rt] = -INFINITY;
+                bz[rt] = 0.f;
+            }
+            for (int sub = 0; sub < NSUB; ++sub) {
+                const int j0 = J * C + sub * 16;
+                const int jr = min(j0 + lr, ns - 1);
+                bf16x8 ka[3][KS];
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        ka[p][ks] = as_bf16x8(ld16(kb + p * plane + (size_t)jr * D + ks * 32 + lg * 8));
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    if (rt >= NT) break;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int p = 0; p < 3; ++p)
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(ka[p][ks], qf[rt][ks], acc);
+                    float s[4], tm = -INFINITY;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = j0 + lg * 4 + e;
+                        s[e] = (j <= row_i[rt]) ? acc[e] * scale2 : -INFINITY;
+                        tm = fmaxf(tm, s[e]);
+                    }
+                    tm = fmaxf(tm, xor_lane(tm, 16));
+                    tm = fmaxf(tm, xor_lane(tm, 32));
+                    const float nm = fmaxf(bm[rt], tm);
+                    if (nm != -INFINITY) {
+                        float z = (bm[rt] == -INFINITY) ? 0.f : bz[rt] * fast_exp2(bm[rt] - nm);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (s[e] != -INFINITY) z += fast_exp2(s[e] - nm);
+                        bz[rt] = z;
+                        bm[rt] = nm;
+                    }
+                }
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                if (rt >= NT) break;
+                float z = bz[rt];
+                z += xor_lane(z, 16);
+                z += xor_lane(z, 32);
+                if (lg == 0 && row_i[rt] >= 0) {
+                    const int a = row_i[rt] - I * C;
+                    stats[(size_t)row_h[rt] * P + packed_row_offset(C, I, a) + J] = make_float2(bm[rt], z);
+                    merge_max_sum(rM[rt], rZ[rt], bm[rt], z);
+                }
+            }
+        } else {
+            constexpr int KPB = C < 4 ? C : 4;  // keys of one block held by a lane
+            constexpr int BPL = 4 / KPB;        // blocks per lane
+            const int j0 = u * 16;
+            const int jr = min(j0 + lr, ns - 1);
+            bf16x8 ka[3][KS];
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    ka[p][ks] = as_bf16x8(ld16(kb + p * plane + (size_t)jr * D + ks * 32 + lg * 8));
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                if (rt >= NT) break;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(ka[p][ks], qf[rt][ks], acc);
+                float s[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = j0 + lg * 4 + e;
+                    s[e] = (j <= row_i[rt]) ? acc[e] * scale2 : -INFINITY;
+                }
+#pragma unroll
+                for (int bi = 0; bi < BPL; ++bi) {
+                    float m = -INFINITY;
+#pragma unroll
+                    for (int e = bi * KPB; e < (bi + 1) * KPB; ++e) m = fmaxf(m, s[e]);
+                    if constexpr (C == 8) m = fmaxf(m, xor_lane(m, 16));
+                    float z = 0.f;
+                    if (m != -INFINITY) {
+#pragma unroll
+                        for (int e = bi * KPB; e < (bi + 1) * KPB; ++e)
+                            if (s[e] != -INFINITY) z += fast_exp2(s[e] - m);
+                    }
+                    if constexpr (C == 8) z += xor_lane(z, 16);
+                    const int J = (j0 + lg * 4 + bi * KPB) / C;
+                    const bool writer = (C == 8) ? ((lg & 1) == 0) : true;
+                    if (writer && row_i[rt] >= 0 && m != -INFINITY) {
+                        const int a = row_i[rt] - I * C;
+                        stats[(size_t)row_h[rt] * P + packed_row_offset(C, I, a) + J] = make_float2(m, z);
+                        merge_max_sum(rM[rt], rZ[rt], m, z);
+                    }
+                }
+            }
+        }
+    }
+
+    // Per-row totals: butterfly over the four lane groups, then across waves.
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        float m2 = xor_lane(rM[rt], 16), z2 = xor_lane(rZ[rt], 16);
+        merge_max_sum(rM[rt], rZ[rt], m2, z2);
+        m2 = xor_lane(rM[rt], 32);
+        z2 = xor_lane(rZ[rt], 32);
+        merge_max_sum(rM[rt], rZ[rt], m2, z2);
+    }
+    __shared__ float2 red[4][64];
+    if (lg == 0) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) red[wid][rt * 16 + lr] = make_float2(rM[rt], rZ[rt]);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int r = threadIdx.x;
+        float M = -INFINITY, Z = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) merge_max_sum(M, Z, red[w][r].x, red[w][r].y);
+        const int f = chunk * 64 + r;
+        const int hh = f / C, a = f % C;
+        if (r < rows_here && hh < G && a < cI)
+            rowstat[(size_t)(g * G + hh) * ns + I * C + a] = make_float2(M, Z);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// rr_stride_softmax_pool: one work-group per (block-row I, query head h).
+// A[h][I][J] = sum_a z(a,J) 2^(m(a,J) - M_a) / Z_a over the strides a of
+// block I, i.e. the causal softmax of each sampled row summed over the
+// block's strides.  Threads walk J, so each (row, J) pair is read once and
+// coalesced.  Entries J > I are written as zero.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rr_stride_softmax_pool(const float2 *__restrict__ stats,
+                                                              const float2 *__restrict__ rowstat,
+                                                              int C, int nb, int ns, long long P,
+                                                              float *__restrict__ A) {
+    const int I = blockIdx.x, h = blockIdx.y;
+    const int cI = min(C, ns - I * C);
+    __shared__ float sM[128], sInvZ[128];
+    for (int a = threadIdx.x; a < cI; a += blockDim.x) {
+        float2 rs = rowstat[(size_t)h * ns + I * C + a];
+        sM[a] = rs.x;
+        sInvZ[a] = 1.f / rs.y;
+    }
+    __syncthreads();
+    const float2 *base = stats + (size_t)h * P + (long long)C * I * (I + 1) / 2;
+    float *out = A + ((size_t)h * nb + I) * nb;
+    for (int J = threadIdx.x; J < nb; J += blockDim.x) {
+        float acc = 0.f;
+        if (J <= I) {
+            for (int a = 0; a < cI; ++a) {
+                const float2 st = base[(size_t)a * (I + 1) + J];
+                acc += st.y * fast_exp2(st.x - sM[a]) * sInvZ[a];
+            }
+        }
+        out[J] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_pool_k(const uint16_t *K, const Shape &s, uint16_t *kplanes, hipStream_t st) {
+    const long long total = (long long)s.ns * s.Hkv * (s.d / 8);
+    const unsigned grid = (unsigned)((total + 255) / 256);
+    const float invS = 1.f / (float)s.S;
+    if (s.d == 128)
+        hipLaunchKernelGGL(rr_pool_k<128>, dim3(grid), dim3(256), 0, st, K, s.Hkv, s.ns, s.S, invS, kplanes);
+    else
+        hipLaunchKernelGGL(rr_pool_k<64>, dim3(grid), dim3(256), 0, st, K, s.Hkv, s.ns, s.S, invS, kplanes);
+    return hipGetLastError();
+}
+
+template <int D>
+static void launch_score_d(const uint16_t *Q, const Shape &s, const EstimateWs &w, hipStream_t st) {
+    const int nchunks = (s.G * s.c + 63) / 64;
+    const dim3 grid((unsigned)(s.nb * s.Hkv * nchunks));
+    const float scale2 = kLog2e / sqrtf((float)D);
+#define RR_SCORE_CASE(CC)                                                                      \
+    case CC:                                                                                   \
+        hipLaunchKernelGGL((rr_score<D, CC>), grid, dim3(256), 0, st, Q, w.kplanes, s.Hq, s.Hkv, \
+                           s.S, s.nb, s.ns, s.G, nchunks, s.P, scale2, w.stats, w.rowstat);    \
+        break;
+    switch (s.c) {
+        RR_SCORE_CASE(1)
+        RR_SCORE_CASE(2)
+        RR_SCORE_CASE(4)
+        RR_SCORE_CASE(8)
+        RR_SCORE_CASE(16)
+        RR_SCORE_CASE(32)
+        RR_SCORE_CASE(64)
+        RR_SCORE_CASE(128)
+        default: break;
+    }
+#undef RR_SCORE_CASE
+}
+
+hipError_t launch_score(const uint16_t *Q, const Shape &s, const EstimateWs &w, hipStream_t st) {
+    if (s.d == 128)
+        launch_score_d<128>(Q, s, w, st);
+    else
+        launch_score_d<64>(Q, s, w, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_softmax_pool(const Shape &s, const EstimateWs &w, float *A, hipStream_t st) {
+    hipLaunchKernelGGL(rr_stride_softmax_pool, dim3(s.nb, s.Hq), dim3(256), 0, st, w.stats,
+                       w.rowstat, s.c, s.nb, s.ns, s.P, A);
+    return hipGetLastError();
+}
+
+}  // namespace rr

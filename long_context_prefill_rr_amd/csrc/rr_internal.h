@@ -1,0 +1,75 @@
+// rr_internal.h -- host-side layout helpers and kernel launchers of librr.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rr {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Shape of one call, with the derived sizes every stage uses.
+struct Shape {
+    int L, Hq, Hkv, d, B, S;
+    int G;    // query heads per kv-head
+    int nb;   // ceil(L / B) blocks
+    int ns;   // L / S strides
+    int c;    // B / S strides per block
+    int c_last;        // strides in the last block
+    long long P;       // packed (row, key-block) entries per head
+};
+
+inline Shape make_shape(int L, int Hq, int Hkv, int d, int B, int S) {
+    Shape s;
+    s.L = L; s.Hq = Hq; s.Hkv = Hkv; s.d = d; s.B = B; s.S = S;
+    s.G = Hq / Hkv;
+    s.nb = (L + B - 1) / B;
+    s.ns = L / S;
+    s.c = B / S;
+    s.c_last = s.ns - (s.nb - 1) * s.c;
+    s.P = (long long)s.c * (s.nb - 1) * s.nb / 2 + (long long)s.c_last * s.nb;
+    return s;
+}
+
+// Estimation workspace: pooled-key planes, per-(row, key-block) (max, sum)
+// pairs and per-row (max, sum) pairs.
+struct EstimateWs {
+    uint16_t *kplanes;  // [3][Hkv][ns][d] bf16 (hi, mid, lo split of the fp32 mean)
+    float2 *stats;      // [Hq][P] packed, row i = I*c + a owns entries J = 0..I
+    float2 *rowstat;    // [Hq][ns]
+};
+
+inline size_t estimate_ws_bytes(const Shape &s) {
+    return align_up((size_t)3 * s.Hkv * s.ns * s.d * 2) + align_up((size_t)s.Hq * s.P * 8) +
+           align_up((size_t)s.Hq * s.ns * 8);
+}
+
+inline EstimateWs carve_estimate(const Shape &s, void *ws) {
+    EstimateWs w;
+    char *p = (char *)ws;
+    w.kplanes = (uint16_t *)p;
+    p += align_up((size_t)3 * s.Hkv * s.ns * s.d * 2);
+    w.stats = (float2 *)p;
+    p += align_up((size_t)s.Hq * s.P * 8);
+    w.rowstat = (float2 *)p;
+    return w;
+}
+
+// Attention workspace: V transposed to [Hkv][d][nb*B] (zero-padded tail).
+inline size_t attn_ws_bytes(const Shape &s) { return align_up((size_t)s.Hkv * s.d * s.nb * s.B * 2); }
+
+// Launchers (enqueue on `stream`, return the launch error).
+hipError_t launch_pool_k(const uint16_t *K, const Shape &s, uint16_t *kplanes, hipStream_t st);
+hipError_t launch_score(const uint16_t *Q, const Shape &s, const EstimateWs &w, hipStream_t st);
+hipError_t launch_softmax_pool(const Shape &s, const EstimateWs &w, float *A, hipStream_t st);
+hipError_t launch_topk_tau(const float *A, const Shape &s, float tau, int32_t *counts,
+                           int32_t *block_idx, hipStream_t st);
+hipError_t launch_transpose_v(const uint16_t *V, const Shape &s, uint16_t *Vt, hipStream_t st);
+hipError_t launch_block_sparse_fa(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt,
+                                  const Shape &s, const int32_t *counts, const int32_t *block_idx,
+                                  void *O, bool out_f32, hipStream_t st);
+
+}  // namespace rr

@@ -1,0 +1,189 @@
+"""ctypes binding of librr.so: the same four calls as the C ABI (include/rr.h).
+
+Every function only checks tensor placement, dtype and contiguity, allocates
+outputs and workspace with torch when the caller does not pass them, and
+forwards device pointers plus the current HIP stream.  All arithmetic runs in
+the library's kernels.
+
+Layouts: q [L][Hq][d], k and v [L][Hkv][d], all torch.bfloat16 on the GPU.
+"""
+import ctypes
+import os
+
+import torch
+
+RR_OUT_BF16 = 0
+RR_OUT_F32 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "librr.so")
+_lib = None
+
+_STATUS = {0: "RR_OK", 1: "RR_E_NULL", 2: "RR_E_SHAPE", 3: "RR_E_TAU", 4: "RR_E_WORKSPACE",
+           5: "RR_E_UNSUPPORTED", 6: "RR_E_HIP"}
+
+
+class RRError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        msg = _load().rr_status_str(code).decode() if _lib is not None else _STATUS.get(code, "?")
+        super().__init__("%s: %s (status %d)" % (where, msg, code))
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load librr.so (raises if it has not been built)."""
+    return _load()
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("librr.so not found at %s: build it with "
+                              "`python -m long_context_prefill_rr_amd.build`" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, i, z, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+        lib.rr_status_str.argtypes = [i]
+        lib.rr_status_str.restype = ctypes.c_char_p
+        lib.rr_abi_version.restype = i
+        lib.rr_estimate_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        lib.rr_estimate_workspace_bytes.restype = z
+        lib.rr_sparse_attn_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.rr_sparse_attn_workspace_bytes.restype = z
+        lib.rr_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        lib.rr_prefill_workspace_bytes.restype = z
+        lib.rr_estimate.argtypes = [P, P, i, i, i, i, i, i, P, P, z, P]
+        lib.rr_select.argtypes = [P, i, i, i, f, P, P, P]
+        lib.rr_sparse_attn.argtypes = [P, P, P, i, i, i, i, i, P, P, P, i, P, z, P]
+        lib.rr_prefill.argtypes = [P, P, P, i, i, i, i, i, i, f, P, i, P, P, P, z, P]
+        for name in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill"):
+            getattr(lib, name).restype = i
+        _lib = lib
+    return _lib
+
+
+def _stream_ptr(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must have dtype %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(rc, where):
+    if rc != 0:
+        raise RRError(rc, where)
+
+
+def estimate_workspace_bytes(L, Hq, Hkv, d, B, S):
+    return _load().rr_estimate_workspace_bytes(L, Hq, Hkv, d, B, S)
+
+
+def sparse_attn_workspace_bytes(L, Hq, Hkv, d, B):
+    return _load().rr_sparse_attn_workspace_bytes(L, Hq, Hkv, d, B)
+
+
+def prefill_workspace_bytes(L, Hq, Hkv, d, B, S):
+    return _load().rr_prefill_workspace_bytes(L, Hq, Hkv, d, B, S)
+
+
+def _workspace(nbytes, device, ws):
+    if ws is None:
+        return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError("workspace too small: %d < %d bytes" % (ws.numel() * ws.element_size(), nbytes))
+    return ws
+
+
+def rr_estimate(q, k, B, S, block_scores=None, ws=None, stream=None):
+    """Block scores [Hq][nb][nb] (fp32) of the round-robin estimate."""
+    L, Hq, d = q.shape
+    Hkv = k.shape[1]
+    nb = -(-L // B)
+    if block_scores is None:
+        block_scores = torch.empty((Hq, nb, nb), dtype=torch.float32, device=q.device)
+    lib = _load()
+    ws = _workspace(lib.rr_estimate_workspace_bytes(L, Hq, Hkv, d, B, S), q.device, ws)
+    rc = lib.rr_estimate(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), L, Hq, Hkv,
+                         d, B, S, _dev(block_scores, "block_scores", torch.float32),
+                         _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream_ptr(stream))
+    _check(rc, "rr_estimate")
+    return block_scores
+
+
+def rr_select(block_scores, L, B, tau, counts=None, block_idx=None, stream=None):
+    """Top-tau selection: (counts [Hq][nb], block_idx [Hq][nb][nb]) int32."""
+    Hq, nb, _ = block_scores.shape
+    dev = block_scores.device
+    if counts is None:
+        counts = torch.empty((Hq, nb), dtype=torch.int32, device=dev)
+    if block_idx is None:
+        block_idx = torch.empty((Hq, nb, nb), dtype=torch.int32, device=dev)
+    rc = _load().rr_select(_dev(block_scores, "block_scores", torch.float32), Hq, L, B,
+                           float(tau), _dev(counts, "counts", torch.int32),
+                           _dev(block_idx, "block_idx", torch.int32), _stream_ptr(stream))
+    _check(rc, "rr_select")
+    return counts, block_idx
+
+
+def _out_code(out_dtype):
+    if out_dtype == torch.float32:
+        return RR_OUT_F32
+    if out_dtype == torch.bfloat16:
+        return RR_OUT_BF16
+    raise TypeError("output dtype must be float32 or bfloat16")
+
+
+def rr_sparse_attn(q, k, v, B, counts, block_idx, out=None, out_dtype=torch.float32, ws=None,
+                   stream=None):
+    """Causal block-sparse GQA attention over the listed blocks -> O [L][Hq][d]."""
+    L, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if out is None:
+        out = torch.empty((L, Hq, d), dtype=out_dtype, device=q.device)
+    code = _out_code(out.dtype)
+    lib = _load()
+    ws = _workspace(lib.rr_sparse_attn_workspace_bytes(L, Hq, Hkv, d, B), q.device, ws)
+    rc = lib.rr_sparse_attn(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
+                            _dev(v, "v", torch.bfloat16), L, Hq, Hkv, d, B,
+                            _dev(counts, "counts", torch.int32),
+                            _dev(block_idx, "block_idx", torch.int32), _dev(out, "out"), code,
+                            _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream_ptr(stream))
+    _check(rc, "rr_sparse_attn")
+    return out
+
+
+def rr_prefill(q, k, v, B, S, tau, out=None, out_dtype=torch.bfloat16, counts=None,
+               block_idx=None, ws=None, stream=None):
+    """The whole sparse prefill: returns (O, counts, block_idx)."""
+    L, Hq, d = q.shape
+    Hkv = k.shape[1]
+    nb = -(-L // B)
+    dev = q.device
+    if out is None:
+        out = torch.empty((L, Hq, d), dtype=out_dtype, device=dev)
+    if counts is None:
+        counts = torch.empty((Hq, nb), dtype=torch.int32, device=dev)
+    if block_idx is None:
+        block_idx = torch.empty((Hq, nb, nb), dtype=torch.int32, device=dev)
+    code = _out_code(out.dtype)
+    lib = _load()
+    ws = _workspace(lib.rr_prefill_workspace_bytes(L, Hq, Hkv, d, B, S), dev, ws)
+    rc = lib.rr_prefill(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
+                        _dev(v, "v", torch.bfloat16), L, Hq, Hkv, d, B, S, float(tau),
+                        _dev(out, "out"), code, _dev(counts, "counts", torch.int32),
+                        _dev(block_idx, "block_idx", torch.int32), _dev(ws, "ws"),
+                        ws.numel() * ws.element_size(), _stream_ptr(stream))
+    _check(rc, "rr_prefill")
+    return out, counts, block_idx

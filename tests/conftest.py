@@ -12,6 +12,13 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
 
 
+def pytest_runtest_setup(item):
+    if item.get_closest_marker("gpu") is not None:
+        import torch
+        if not torch.cuda.is_available():
+            pytest.skip("no GPU visible")
+
+
 @pytest.fixture(scope="session", autouse=True)
 def _oracle_built():
     import oracle

@@ -1,0 +1,83 @@
+"""Comparison rules between the GPU path and the oracle (test logic only).
+
+Mask rule: for each (head, block-row) the GPU's kept set must equal the
+oracle's, except for blocks whose cumulative boundary lies within 1e-4 of tau
+(the oracle's normalised mass ordered before the block, |C_before - tau| <=
+1e-4).  Differences outside that band are split into "tie" (the block traded
+places with another differing block of the same row whose normalised oracle
+score is within TIE_GAP) and "unexcused".
+"""
+import numpy as np
+
+BOUNDARY = 1e-4
+TIE_GAP = 1e-6
+
+
+def classify_masks(keep_gpu, keep_orc, cbefore, A_orc, tau, valid_rows=None):
+    """Return dict(match_rows, rows, diff_blocks, boundary, tie, unexcused, examples)."""
+    keep_gpu = np.asarray(keep_gpu).astype(bool)
+    keep_orc = np.asarray(keep_orc).astype(bool)
+    nb = keep_orc.shape[-1]
+    kg = keep_gpu.reshape(-1, nb)
+    ko = keep_orc.reshape(-1, nb)
+    cb = np.asarray(cbefore).reshape(-1, nb)
+    A = np.asarray(A_orc, dtype=np.float64).reshape(-1, nb)
+    out = dict(rows=kg.shape[0], match_rows=0, diff_blocks=0, boundary=0, tie=0, unexcused=0,
+               examples=[])
+    W = A.sum(axis=1)
+    diff = kg != ko
+    out["match_rows"] = int((~diff.any(axis=1)).sum())
+    for r in np.nonzero(diff.any(axis=1))[0]:
+        Js = np.nonzero(diff[r])[0]
+        an = A[r] / W[r]
+        for J in Js:
+            out["diff_blocks"] += 1
+            if abs(cb[r, J] - tau) <= BOUNDARY:
+                out["boundary"] += 1
+                continue
+            others = [J2 for J2 in Js if J2 != J and ko[r, J2] != ko[r, J]]
+            if any(abs(an[J] - an[J2]) <= TIE_GAP for J2 in others):
+                out["tie"] += 1
+                continue
+            out["unexcused"] += 1
+            if len(out["examples"]) < 5:
+                out["examples"].append((int(r), int(J), float(cb[r, J]), float(an[J])))
+    return out
+
+
+def mask_from_list(counts, idx, nb):
+    """Dense mask from a compacted (counts, ascending indices) list, vectorised."""
+    counts = np.asarray(counts)
+    idx = np.asarray(idx)
+    Hq = counts.shape[0]
+    pos = np.arange(nb)[None, None, :]
+    valid = pos < counts[:, :, None]
+    m = np.zeros((Hq, nb, nb), dtype=np.uint8)
+    hh, II, kk = np.nonzero(valid)
+    m[hh, II, idx[hh, II, kk]] = 1
+    return m
+
+
+def list_is_well_formed(counts, idx):
+    """Ascending, in range J <= I, non-empty, -1 padded."""
+    counts = np.asarray(counts)
+    idx = np.asarray(idx)
+    Hq, nb = counts.shape
+    pos = np.arange(nb)[None, None, :]
+    valid = pos < counts[:, :, None]
+    if np.any(counts < 1) or np.any(counts > np.arange(1, nb + 1)[None, :]):
+        return False
+    if np.any(idx[~valid] != -1):
+        return False
+    v = np.where(valid, idx, 10 ** 9)
+    if np.any(v[valid] < 0):
+        return False
+    if np.any((v <= np.arange(nb)[None, :, None]) != valid):
+        return False
+    d = np.diff(np.where(valid, idx, np.iinfo(np.int32).max), axis=2)
+    return bool(np.all(d[valid[:, :, 1:]] > 0))
+
+
+def o_errors(o_gpu, o_ref):
+    e = np.abs(np.asarray(o_gpu, dtype=np.float64) - np.asarray(o_ref, dtype=np.float64))
+    return float(e.max()), float(e.mean())

@@ -1,0 +1,114 @@
+"""The C-ABI library loads, exports every symbol include/rr.h declares, and
+rejects bad arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rr.h")
+LIB = os.path.join(ROOT, "long_context_prefill_rr_amd", "librr.so")
+
+RR_OK, RR_E_NULL, RR_E_SHAPE, RR_E_TAU, RR_E_WORKSPACE, RR_E_UNSUPPORTED = 0, 1, 2, 3, 4, 5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rr_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from long_context_prefill_rr_amd import build
+        build.build()
+    from long_context_prefill_rr_amd import rr
+    return rr.load_library()
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        getattr(lib, n)
+
+
+def test_status_strings(lib):
+    for c in range(7):
+        assert lib.rr_status_str(c)
+    assert lib.rr_abi_version() == 1
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _est(lib, L=1024, Hq=8, Hkv=2, d=128, B=128, S=8, ws_bytes=1 << 40, Q=FAKE):
+    return lib.rr_estimate(Q, FAKE, L, Hq, Hkv, d, B, S, FAKE, FAKE, ws_bytes, None)
+
+
+def test_estimate_validation(lib):
+    assert _est(lib, Q=None) == RR_E_NULL
+    assert _est(lib, L=1004) == RR_E_SHAPE           # L % S
+    assert _est(lib, L=0) == RR_E_SHAPE
+    assert _est(lib, Hq=6, Hkv=4) == RR_E_SHAPE      # Hq % Hkv
+    assert _est(lib, S=256) == RR_E_SHAPE            # S > B
+    assert _est(lib, S=12) == RR_E_SHAPE             # B % S
+    assert _est(lib, d=96) == RR_E_UNSUPPORTED
+    assert _est(lib, B=256, S=8) == RR_E_UNSUPPORTED
+    assert _est(lib, ws_bytes=16) == RR_E_WORKSPACE
+    assert _est(lib, L=128 * 4097) == RR_E_UNSUPPORTED
+
+
+def test_workspace_sizes(lib):
+    assert lib.rr_estimate_workspace_bytes(1004, 8, 2, 128, 128, 8) == 0
+    a = lib.rr_estimate_workspace_bytes(8192, 32, 8, 128, 128, 8)
+    b = lib.rr_sparse_attn_workspace_bytes(8192, 32, 8, 128, 128)
+    c = lib.rr_prefill_workspace_bytes(8192, 32, 8, 128, 128, 8)
+    assert a > 0 and b > 0 and c >= max(a, b) + 32 * 64 * 64 * 4
+    # pooled-key planes + packed (row, block) pairs + row pairs
+    ns, nb, c16 = 1024, 64, 16
+    P = c16 * nb * (nb + 1) // 2
+    assert a >= 3 * 8 * ns * 128 * 2 + 32 * P * 8 + 32 * ns * 8
+
+
+def test_select_and_attn_validation(lib):
+    f = ctypes.c_float
+    assert lib.rr_select(FAKE, 8, 1024, 128, f(0.0), FAKE, FAKE, None) == RR_E_TAU
+    assert lib.rr_select(FAKE, 8, 1024, 128, f(1.5), FAKE, FAKE, None) == RR_E_TAU
+    assert lib.rr_select(FAKE, 8, 1024, 128, f(float("nan")), FAKE, FAKE, None) == RR_E_TAU
+    assert lib.rr_select(None, 8, 1024, 128, f(0.9), FAKE, FAKE, None) == RR_E_NULL
+    assert lib.rr_select(FAKE, 0, 1024, 128, f(0.9), FAKE, FAKE, None) == RR_E_SHAPE
+    args = [FAKE, FAKE, FAKE, 1024, 8, 2, 128, 128, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40, None]
+    a = list(args); a[11] = 7
+    assert lib.rr_sparse_attn(*a) == RR_E_UNSUPPORTED       # bad output dtype
+    a = list(args); a[13] = 1
+    assert lib.rr_sparse_attn(*a) == RR_E_WORKSPACE
+    a = list(args); a[0] = None
+    assert lib.rr_sparse_attn(*a) == RR_E_NULL
+    pf = [FAKE, FAKE, FAKE, 1024, 8, 2, 128, 128, 8, f(0.9), FAKE, 1, FAKE, FAKE, FAKE, 1 << 40, None]
+    p = list(pf); p[9] = f(-0.1)
+    assert lib.rr_prefill(*p) == RR_E_TAU
+    p = list(pf); p[8] = 3
+    assert lib.rr_prefill(*p) == RR_E_SHAPE
+    p = list(pf); p[15] = 10
+    assert lib.rr_prefill(*p) == RR_E_WORKSPACE
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    from long_context_prefill_rr_amd import rr
+    q = torch.zeros((128, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        rr.rr_estimate(q, q, 64, 8)

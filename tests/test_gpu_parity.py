@@ -1,0 +1,216 @@
+"""GPU parity: librr (through its C ABI) against the fp64 oracle.
+
+Rules (tests/parity.py): block masks equal the oracle's except for blocks
+whose cumulative boundary is within 1e-4 of tau; attention outputs computed
+under the oracle's mask are within max |err| 1e-2 and mean |err| 1e-3 (fp32
+output); block scores agree to BLOCK_SCORE_TOL after division by the row
+total.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rr_workloads import generate
+from tests.helpers import small_workload
+from tests.parity import classify_masks, list_is_well_formed, mask_from_list, o_errors
+
+pytestmark = pytest.mark.gpu
+
+# |A_gpu - A_oracle| / W.  Scores carry ~1e-6 relative error from fp32
+# accumulation of the three-plane products and from v_exp_f32; a block score
+# is a sum of probabilities, so its error stays below ~1e-5 of the row total.
+BLOCK_SCORE_TOL = 1e-5
+O_MAX, O_MEAN = 1e-2, 1e-3
+
+
+def _rr():
+    import long_context_prefill_rr_amd as rr
+    rr.load_library()
+    return rr
+
+
+def _dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+SMALL = [
+    # (kind, L, Hq, Hkv, d, B, S, tau)
+    ("llama", 1216, 8, 2, 128, 128, 8, 0.9),   # ragged last block
+    ("llama", 1024, 8, 2, 128, 128, 16, 0.8),
+    ("tiny", 640, 4, 4, 64, 64, 4, 0.9),       # G = 1, ragged
+    ("video", 2048, 7, 1, 128, 128, 16, 0.95),  # G = 7
+    ("llama", 320, 4, 1, 64, 64, 1, 0.9),      # S = 1: every token sampled
+    ("llama", 512, 4, 2, 64, 64, 2, 0.9),
+    ("llama", 512, 4, 2, 128, 64, 32, 0.9),    # c = 2
+    ("llama", 512, 4, 2, 128, 64, 64, 0.9),    # c = 1
+    ("llama", 1024, 6, 3, 64, 128, 8, 0.5),
+]
+
+
+def _case(kind, L, Hq, Hkv, d, B, S, tau, seed=11):
+    w, g = small_workload(kind=kind, L=L, Hq=Hq, Hkv=Hkv, d=d, B=B, S=S, seed=seed)
+    return w.with_params(tau=tau), g
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[str(c) for c in SMALL])
+def test_estimate_matches_oracle(case):
+    rr = _rr()
+    w, g = _case(*case)
+    _note("estimate %s" % (case,))
+    A_orc = oracle.block_scores(g["q"], g["k"], w.B, w.S)
+    A = rr.rr_estimate(_dev(g["q"]), _dev(g["k"]), w.B, w.S)
+    torch.cuda.synchronize()
+    A = A.cpu().numpy().astype(np.float64)
+    W = A_orc.sum(axis=2, keepdims=True)
+    err = np.abs(A - A_orc) / W
+    _note("  max |dA|/W = %.3g" % err.max())
+    assert err.max() <= BLOCK_SCORE_TOL
+    assert np.all(np.triu(A, 1) == 0)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[str(c) for c in SMALL])
+def test_select_on_oracle_scores(case):
+    rr = _rr()
+    w, g = _case(*case)
+    _note("select %s" % (case,))
+    A_orc = oracle.block_scores(g["q"], g["k"], w.B, w.S)
+    keep_o, cnt_o, cb = oracle.select(A_orc, w.tau)
+    A32 = torch.from_numpy(A_orc.astype(np.float32)).cuda()
+    counts, idx = rr.rr_select(A32, w.L, w.B, w.tau)
+    torch.cuda.synchronize()
+    counts, idx = counts.cpu().numpy(), idx.cpu().numpy()
+    assert list_is_well_formed(counts, idx)
+    res = classify_masks(mask_from_list(counts, idx, w.nb), keep_o, cb, A_orc, w.tau)
+    _note("  %s" % res)
+    assert res["unexcused"] == 0 and res["tie"] == 0
+
+
+def test_select_hand_worked_cases():
+    # Dyadic scores from tests/golden/find_blocks_hand.txt are exact in fp32.
+    import os
+    rr = _rr()
+    path = os.path.join(os.path.dirname(__file__), "golden", "find_blocks_hand.txt")
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        tau, scores, kept = [p.strip() for p in line.split("|")]
+        a = np.array([float(x) for x in scores.split()], dtype=np.float32)
+        n = a.shape[0]
+        A = np.zeros((1, n, n), dtype=np.float32)
+        A[0, n - 1] = a
+        for I in range(n - 1):
+            A[0, I, :I + 1] = 1.0
+        counts, idx = rr.rr_select(torch.from_numpy(A).cuda(), n * 64, 64, float(tau))
+        got = idx[0, n - 1, :counts[0, n - 1]].cpu().tolist()
+        assert got == [int(x) for x in kept.split()], line
+
+
+@pytest.mark.parametrize("case", SMALL[:4] + SMALL[5:6], ids=[str(c) for c in SMALL[:4] + SMALL[5:6]])
+@pytest.mark.parametrize("maskkind", ["oracle", "dense", "random"])
+def test_sparse_attn_matches_oracle(case, maskkind):
+    rr = _rr()
+    w, g = _case(*case)
+    _note("sparse_attn %s %s" % (case, maskkind))
+    nb = w.nb
+    if maskkind == "oracle":
+        A_orc = oracle.block_scores(g["q"], g["k"], w.B, w.S)
+        mask, _, _ = oracle.select(A_orc, w.tau)
+    elif maskkind == "dense":
+        mask = np.broadcast_to(np.tril(np.ones((nb, nb), np.uint8)), (w.Hq, nb, nb)).copy()
+    else:
+        rng = np.random.default_rng(5)
+        mask = np.tril((rng.uniform(size=(w.Hq, nb, nb)) < 0.4).astype(np.uint8))
+        for h in range(w.Hq):
+            for I in range(nb):
+                if not mask[h, I].any():
+                    mask[h, I, rng.integers(0, I + 1)] = 1
+    counts, idx = oracle.list_from_mask(mask)
+    idx = np.where(np.arange(nb)[None, None, :] < counts[:, :, None], idx, -1).astype(np.int32)
+    O_orc = oracle.attention(g["q"], g["k"], g["v"], w.B, mask)
+    q, k, v = _dev(g["q"]), _dev(g["k"]), _dev(g["v"])
+    c_t, i_t = torch.from_numpy(counts).cuda(), torch.from_numpy(idx).cuda()
+    O = rr.rr_sparse_attn(q, k, v, w.B, c_t, i_t, out_dtype=torch.float32)
+    Ob = rr.rr_sparse_attn(q, k, v, w.B, c_t, i_t, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    mx, mean = o_errors(O.cpu().numpy(), O_orc)
+    mxb, meanb = o_errors(Ob.float().cpu().numpy(), O_orc)
+    _note("  f32 max %.3g mean %.3g | bf16 max %.3g mean %.3g" % (mx, mean, mxb, meanb))
+    assert mx <= O_MAX and mean <= O_MEAN
+    assert mxb <= 2 * O_MAX  # bf16 output rounding adds up to half a bf16 ulp
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[str(c) for c in SMALL])
+def test_prefill_end_to_end(case):
+    rr = _rr()
+    w, g = _case(*case)
+    _note("prefill %s" % (case,))
+    A_orc = oracle.block_scores(g["q"], g["k"], w.B, w.S)
+    keep_o, _, cb = oracle.select(A_orc, w.tau)
+    q, k, v = _dev(g["q"]), _dev(g["k"]), _dev(g["v"])
+    O, counts, idx = rr.rr_prefill(q, k, v, w.B, w.S, w.tau, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    counts, idx = counts.cpu().numpy(), idx.cpu().numpy()
+    assert list_is_well_formed(counts, idx)
+    mask = mask_from_list(counts, idx, w.nb)
+    res = classify_masks(mask, keep_o, cb, A_orc, w.tau)
+    _note("  mask %s" % res)
+    assert res["unexcused"] == 0
+    O_ref = oracle.attention(g["q"], g["k"], g["v"], w.B, mask)
+    mx, mean = o_errors(O.cpu().numpy(), O_ref)
+    _note("  O under GPU mask: max %.3g mean %.3g" % (mx, mean))
+    assert mx <= O_MAX and mean <= O_MEAN
+
+
+def test_tau_one_is_dense_causal():
+    rr = _rr()
+    w, g = _case("llama", 1216, 8, 2, 128, 128, 8, 1.0)
+    q, k, v = _dev(g["q"]), _dev(g["k"]), _dev(g["v"])
+    O, counts, idx = rr.rr_prefill(q, k, v, w.B, w.S, 1.0, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(counts.cpu().numpy(), np.broadcast_to(np.arange(1, w.nb + 1), (w.Hq, w.nb)))
+    dense = np.broadcast_to(np.tril(np.ones((w.nb, w.nb), np.uint8)), (w.Hq, w.nb, w.nb)).copy()
+    O_ref = oracle.attention(g["q"], g["k"], g["v"], w.B, dense)
+    mx, mean = o_errors(O.cpu().numpy(), O_ref)
+    assert mx <= O_MAX and mean <= O_MEAN
+
+
+def test_repeat_runs_are_bitwise_identical():
+    rr = _rr()
+    w, g = _case("llama", 2048, 8, 2, 128, 128, 8, 0.9)
+    q, k, v = _dev(g["q"]), _dev(g["k"]), _dev(g["v"])
+    outs = []
+    for _ in range(2):
+        A = rr.rr_estimate(q, k, w.B, w.S)
+        O, counts, idx = rr.rr_prefill(q, k, v, w.B, w.S, w.tau, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        outs.append((A.cpu().numpy(), O.cpu().numpy(), counts.cpu().numpy(), idx.cpu().numpy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+
+
+def test_non_default_stream_and_errors():
+    rr = _rr()
+    w, g = _case("llama", 512, 4, 2, 64, 64, 8, 0.9)
+    q, k, v = _dev(g["q"]), _dev(g["k"]), _dev(g["v"])
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        O1, c1, i1 = rr.rr_prefill(q, k, v, w.B, w.S, w.tau, out_dtype=torch.float32, stream=s)
+    s.synchronize()
+    O2, c2, i2 = rr.rr_prefill(q, k, v, w.B, w.S, w.tau, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(c1, c2) and torch.equal(i1, i2)
+    with pytest.raises(rr.RRError) as e:
+        rr.rr_prefill(q, k, v, w.B, 3, w.tau)
+    assert e.value.code in (2, 5)
+    with pytest.raises(rr.RRError) as e:
+        rr.rr_prefill(q, k, v, w.B, w.S, 1.5)
+    assert e.value.code == 3
