@@ -7,9 +7,12 @@
 // 1/sqrt(d), and query head h reads kv-head h / (Hq/Hkv) (GQA).
 //
 // Work-group = one (query head h, query block I): BLK/32 waves, each owning 32
-// query rows.  Per kept key block J (ascending):
-//   * the K tile [BLK keys][d] and the V^T tile [d][BLK keys] are staged in
-//     LDS (row pitch padded by 16 bytes against bank conflicts);
+// query rows.  Kept key blocks are walked in ascending order in stages of 64
+// keys:
+//   * the K tile [64 keys][d] and the V^T tile [d][64 keys] of the next stage
+//     are copied global -> LDS by global_load_lds_dwordx4 (no registers) into
+//     the second of two buffers while the current stage is computed; rows
+//     are XOR-swizzled in 16-byte slots against LDS bank conflicts;
 //   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16.  The K rows fed to the
 //     matrix unit are permuted so that accumulator register e of lane
 //     (column q, half hk) holds key 16*hk + e of each 32-key sub-tile:
@@ -23,10 +26,11 @@
 // O^T stays in registers (one query column per lane) and is divided by the
 // softmax sum at the end.
 //
-// Grid order: (block-row descending, kv-head), the G query heads of one
-// (I, g) pair adjacent and on the same XCD (work-groups are dealt to the 8
+// Grid order: kv-head major, block-row descending, the G query heads of one
+// (g, I) pair adjacent and on the same XCD (work-groups are dealt to the 8
 // XCDs round-robin), so the K/V tiles they share are served from that XCD's
-// L2; long rows start first.
+// L2 and one kv-head's K/V (64 MiB at 128K) stays in the last-level cache
+// while its rows run; long rows start first.
 #include "rr_device.h"
 #include "rr_internal.h"
 
@@ -53,29 +57,58 @@ __global__ __launch_bounds__(256) void rr_transpose_v(const uint16_t *__restrict
     }
 }
 
+// Tile constants of the attention kernel: 64-key stages, BLK/32 waves.
+template <int D, int BLK>
+struct FaCfg {
+    static constexpr int NW = BLK / 32;                 // waves (32 query rows each)
+    static constexpr int NT = NW * 64;                  // threads
+    static constexpr int KT = 64;                       // keys per pipeline stage
+    static constexpr int SPB = BLK / KT;                // stages per key block
+    static constexpr int CPRK = D / 8;                  // 16-byte chunks per K row
+    static constexpr int IK = KT * CPRK / 64 / NW;      // K copies per wave per stage
+    static constexpr int IV = D * (KT / 8) / 64 / NW;   // V^T copies per wave per stage
+    static constexpr int LPW = IK + IV;                 // copies per wave per stage
+    static constexpr int KBYTES = KT * D * 2;
+    static constexpr int VBYTES = D * KT * 2;
+    static constexpr int NDT = D / 32;
+    static constexpr int NKS = D / 16;
+};
+
+// LDS swizzles (16-byte slot XOR per row) chosen so that the 16 rows read by
+// one 16-lane group of a ds_read_b128 land in 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+    if constexpr (D == 128) return (r & 7) | (((r >> 4) & 1) << 3);
+    else return ((r >> 1) & 3) | (((r >> 4) & 1) << 2);
+}
+__device__ __forceinline__ int swz_v(int r) { return (r >> 1) & 7; }
+
+// Lazy rescaling threshold (log2 units): the running reference maximum is
+// only raised when a new score exceeds it by more than 2^8, so exponentials
+// stay <= 256 and O is rescaled rarely.
+constexpr float kRescaleTh = 8.f;
+
 template <int D, int BLK, bool OUT_F32>
-__global__ __launch_bounds__(BLK * 2) void rr_block_sparse_fa(
+__global__ __launch_bounds__(BLK * 2, 2) void rr_block_sparse_fa(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ Vt,
     int L, int Lp, int Hq, int Hkv, int nb, int nq, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ block_idx, void *__restrict__ O, float scale2) {
-    constexpr int NT = BLK * 2;   // threads
-    constexpr int KP = D + 8;     // K tile pitch (elements)
-    constexpr int VP = BLK + 8;   // V^T tile pitch (elements)
-    constexpr int NSUB = BLK / 32;
-    constexpr int NDT = D / 32;
-    constexpr int NKS = D / 16;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[BLK * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[D * VP];
+    using C = FaCfg<D, BLK>;
+    __shared__ __attribute__((aligned(1024))) char Kb0[C::KBYTES];
+    __shared__ __attribute__((aligned(1024))) char Kb1[C::KBYTES];
+    __shared__ __attribute__((aligned(1024))) char Vb0[C::VBYTES];
+    __shared__ __attribute__((aligned(1024))) char Vb1[C::VBYTES];
 
     const int G = Hq / Hkv;
-    // XCD-aware decode: x = XCD slot, then heads of one (I, g) pair.
+    // Work decode: groups (kv-head g, block-row I) in kv-head-major order with
+    // I descending; the G query heads of a group are consecutive on one XCD.
     const int bx = blockIdx.x;
     const int x = bx & 7, slot = bx >> 3;
     const int hh = slot % G;
     const int qi = (slot / G) * 8 + x;
     if (qi >= nq) return;
-    const int I = nb - 1 - qi / Hkv;
-    const int g = qi % Hkv;
+    const int g = qi / nb;
+    const int I = nb - 1 - qi % nb;
     const int h = g * G + hh;
 
     const int tid = threadIdx.x;
@@ -83,110 +116,163 @@ __global__ __launch_bounds__(BLK * 2) void rr_block_sparse_fa(
     const int col = lane & 31, hk = lane >> 5;
     const int tq = I * BLK + wid * 32 + col;
 
-    bf16x8 qf[NKS];
+    bf16x8 qf[C::NKS];
     {
-        const bool ok = tq < L;
-        const uint16_t *qp = Q + ((size_t)(ok ? tq : 0) * Hq + h) * D + hk * 8;
+        const uint16_t *qp = Q + ((size_t)min(tq, L - 1) * Hq + h) * D + hk * 8;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qf[ks] = ok ? as_bf16x8(ld16(qp + ks * 16)) : as_bf16x8(zero_u4());
+        for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = as_bf16x8(ld16(qp + ks * 16));
     }
 
-    f32x16 o[NDT];
+    f32x16 o[C::NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
     float m = -INFINITY, lsum = 0.f;
 
-    // Key row of the K tile fed as MFMA row r = col: 16*((r>>2)&1) + 4*(r>>3) + (r&3).
+    // MFMA row r = col of the S^T tile reads K row 16*((r>>2)&1) + 4*(r>>3) + (r&3)
+    // of its 32-key sub-tile, so accumulator e of lane (col, hk) is key 16*hk + e.
     const int krow = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
+    const int ksw = swz_k<D>(krow);
+    const int vsw = swz_v(col);
 
-    // A malformed list (count outside [0, nb], index outside [0, I]) must not
-    // read outside K / V^T: such entries are skipped.
     const int cnt = min(max(counts[(size_t)h * nb + I], 0), nb);
     const int32_t *lst = block_idx + ((size_t)h * nb + I) * nb;
-    for (int it = 0; it < cnt; ++it) {
-        const int J = lst[it];
-        if ((unsigned)J > (unsigned)I) continue;  // uniform across the work-group
-        // Stage K tile and V^T tile.
-#pragma unroll
-        for (int cidx = tid; cidx < BLK * D / 8; cidx += NT) {
-            const int r = cidx / (D / 8), c8 = cidx % (D / 8);
-            const int key = J * BLK + r;
-            uint4 v = zero_u4();
-            if (key < L) v = ld16(K + ((size_t)key * Hkv + g) * D + c8 * 8);
-            st16(&Ks[r * KP + c8 * 8], v);
-        }
-#pragma unroll
-        for (int cidx = tid; cidx < D * BLK / 8; cidx += NT) {
-            const int r = cidx / (BLK / 8), c8 = cidx % (BLK / 8);
-            st16(&Vs[r * VP + c8 * 8], ld16(Vt + ((size_t)g * D + r) * Lp + (size_t)J * BLK + c8 * 8));
-        }
-        __syncthreads();
+    const int nst = cnt * C::SPB;
 
-        f32x16 sacc[NSUB];
+    // Key block of stage st, -1 for an out-of-range list entry (skipped).
+    // The index is made provably uniform so the entry comes through a scalar
+    // load: a vector load would share vmcnt with the LDS copies in flight.
+    auto stage_block = [&](int st) -> int {
+        const int it = __builtin_amdgcn_readfirstlane(st / C::SPB);
+        const int J = lst[it];
+        return ((unsigned)J <= (unsigned)I) ? J : -1;
+    };
+
+    // Start the copies of stage st into (kb, vb); returns false if none.
+    auto issue = [&](int st, char *kb, char *vb) -> bool {
+        const int J = stage_block(st);
+        if (J < 0) return false;
+        const int key0 = J * BLK + (st % C::SPB) * C::KT;
 #pragma unroll
-        for (int kt = 0; kt < NSUB; ++kt) {
+        for (int i = 0; i < C::IK; ++i) {
+            const int p = (wid * C::IK + i) * 64 + lane;
+            const int r = p / C::CPRK, sl = p % C::CPRK;
+            const int c = sl ^ swz_k<D>(r);
+            const int key = min(key0 + r, L - 1);
+            g2lds16(K + ((size_t)key * Hkv + g) * D + c * 8, (lds_char *)kb + (wid * C::IK + i) * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < C::IV; ++i) {
+            const int p = (wid * C::IV + i) * 64 + lane;
+            const int r = p >> 3, sl = p & 7;
+            const int c = sl ^ swz_v(r);
+            g2lds16(Vt + ((size_t)g * D + r) * Lp + key0 + c * 8, (lds_char *)vb + (wid * C::IV + i) * 1024);
+        }
+        return true;
+    };
+
+    auto compute = [&](int st, const char *kb, const char *vb) {
+        const int J = stage_block(st);
+        if (J < 0) return;
+        const int key0 = J * BLK + (st % C::SPB) * C::KT;
+        const bool diag = (J == I);
+        if (diag && I * BLK + wid * 32 + 31 < key0) return;  // whole stage above this wave's rows
+
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
-            const uint16_t *kr = &Ks[(kt * 32 + krow) * KP + hk * 8];
+            const char *kr = kb + (kt * 32 + krow) * (D * 2);
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                sacc[kt] = mfma32x32x16(as_bf16x8(ld16(kr + ks * 16)), qf[ks], sacc[kt]);
+            for (int ks = 0; ks < C::NKS; ++ks) {
+                const uint4 a = *reinterpret_cast<const uint4 *>(kr + (((2 * ks + hk) ^ ksw) << 4));
+                sacc[kt] = mfma32x32x16(as_bf16x8(a), qf[ks], sacc[kt]);
+            }
         }
 
         float mx = -INFINITY;
-        const bool diag = (J == I);
+        if (diag) {
 #pragma unroll
-        for (int kt = 0; kt < NSUB; ++kt)
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float s = sacc[kt][e] * scale2;
-                if (diag) {
-                    const int key = J * BLK + kt * 32 + 16 * hk + e;
-                    if (key > tq) s = -INFINITY;
+                for (int e = 0; e < 16; ++e) {
+                    const int key = key0 + kt * 32 + 16 * hk + e;
+                    if (key > tq) sacc[kt][e] = -INFINITY;
                 }
-                sacc[kt][e] = s;
-                mx = fmaxf(mx, s);
-            }
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
         mx = fmaxf(mx, xor_lane(mx, 32));
-        const float mnew = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - mnew);
-        m = mnew;
-        lsum *= alpha;
+        const float mxs = mx * scale2;
+        if (__ballot(mxs > m + kRescaleTh) != 0ull) {
+            const float mn = fmaxf(m, mxs);
+            const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
+            m = mn;
+            lsum *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+            for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+                for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+        }
+        const float nm = -m;
 
 #pragma unroll
-        for (int kt = 0; kt < NSUB; ++kt) {
+        for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm) {
                 uint32_t pk[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float p0 = fast_exp2(sacc[kt][8 * mm + 2 * e] - mnew);
-                    const float p1 = fast_exp2(sacc[kt][8 * mm + 2 * e + 1] - mnew);
-                    lsum += p0 + p1;
+                    const float p0 = fast_exp2(fmaf(sacc[kt][8 * mm + 2 * e], scale2, nm));
+                    const float p1 = fast_exp2(fmaf(sacc[kt][8 * mm + 2 * e + 1], scale2, nm));
                     pk[e] = pack_bf16x2(p0, p1);
+                    // The normaliser sums the same bf16 weights the P.V product uses.
+                    lsum = add_bf16x2(pk[e], lsum);
                 }
                 const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+                const int voff = ((4 * kt + 2 * hk + mm) ^ vsw) << 4;
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const uint16_t *vr = &Vs[(dt * 32 + col) * VP + kt * 32 + 16 * hk + 8 * mm];
-                    o[dt] = mfma32x32x16(as_bf16x8(ld16(vr)), pb, o[dt]);
+                for (int dt = 0; dt < C::NDT; ++dt) {
+                    const uint4 a = *reinterpret_cast<const uint4 *>(vb + (dt * 32 + col) * (C::KT * 2) + voff);
+                    o[dt] = mfma32x32x16(as_bf16x8(a), pb, o[dt]);
                 }
             }
         }
-        __syncthreads();
+    };
+
+    // Two-stage pipeline over statically distinct LDS buffers: the copies of
+    // stage st+1 run while stage st is computed.  Each wave waits for its own
+    // copies with vmcnt, the barrier then publishes all waves' copies.
+    if (nst > 0) issue(0, Kb0, Vb0);
+    for (int st = 0; st < nst; st += 2) {
+        if (st + 1 < nst && issue(st + 1, Kb1, Vb1))
+            wait_vmcnt<C::LPW>();
+        else
+            wait_vmcnt<0>();
+        bar();
+        compute(st, Kb0, Vb0);
+        wait_lgkm0();
+        bar();
+        if (st + 1 >= nst) break;
+        if (st + 2 < nst && issue(st + 2, Kb0, Vb0))
+            wait_vmcnt<C::LPW>();
+        else
+            wait_vmcnt<0>();
+        bar();
+        compute(st + 1, Kb1, Vb1);
+        wait_lgkm0();
+        bar();
     }
 
     const float tot = lsum + xor_lane(lsum, 32);
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
     if (tq >= L) return;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+    for (int dt = 0; dt < C::NDT; ++dt) {
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
             const int d0 = dt * 32 + 8 * e4 + 4 * hk;

@@ -32,6 +32,14 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// acc + lo(x) + hi(x) for a packed bf16 pair (v_dot2c_f32_bf16 against 1.0).
+__device__ __forceinline__ float add_bf16x2(uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
+                                           __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+}
+
 // Two fp32 -> packed bf16x2 (low half = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return (uint32_t)bf16_bits(a) | ((uint32_t)bf16_bits(b) << 16);
@@ -49,6 +57,29 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // Value of lane (lane ^ m) in a 64-wide wave.
 __device__ __forceinline__ float xor_lane(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// 16-byte global -> LDS copy without registers (global_load_lds_dwordx4):
+// lane i of the wave writes lds_wave_base + 16*i; lds_wave_base must be the
+// same for the whole wave.
+__device__ __forceinline__ void g2lds16(const void *src, lds_char *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (<= n pending).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt lgkmcnt(0) only (LDS reads of this wave have returned).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// Work-group barrier without the memory fence of __syncthreads: the caller
+// orders LDS traffic with explicit waits.
+__device__ __forceinline__ void bar() { __builtin_amdgcn_s_barrier(); }
 
 // Merge two (max, sum-of-2^(x-max)) pairs.  (-inf, 0) is the identity.
 __device__ __forceinline__ void merge_max_sum(float &m, float &z, float m2, float z2) {
