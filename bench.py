@@ -118,6 +118,9 @@ def main():
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-rows", type=int, default=16, help="sampled block-rows per head")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, copy q (known size) once: the reference dispatch for "
+                         "scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -199,6 +202,14 @@ def main():
     pe[1].record()
     torch.cuda.synchronize()
     prefill_ms = pe[0].elapsed_time(pe[1]) / args.steps
+
+    if args.copy_calibration:
+        qc = torch.empty_like(q)
+        torch.cuda.synchronize()
+        qc.copy_(q)
+        torch.cuda.synchronize()
+        log("copy calibration: %d bytes read, %d bytes written" % (q.numel() * 2, q.numel() * 2))
+        del qc
 
     flops_kept, n_kept, n_diag = kept_block_flops(counts, idx, L, B, d)
     dense_flops = 4.0 * d * Hq * L * (L + 1) / 2.0

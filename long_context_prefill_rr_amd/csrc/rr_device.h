@@ -40,9 +40,12 @@ __device__ __forceinline__ float add_bf16x2(uint32_t x, float acc) {
                                            __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
 }
 
-// Two fp32 -> packed bf16x2 (low half = a).
+// Two fp32 -> packed bf16x2 (low half = a), one v_cvt_pk_bf16_f32 (RNE).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return (uint32_t)bf16_bits(a) | ((uint32_t)bf16_bits(b) << 16);
+    bf16x2 r;
+    r[0] = (__bf16)a;
+    r[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
