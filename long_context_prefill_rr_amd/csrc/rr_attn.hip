@@ -88,6 +88,18 @@ __device__ __forceinline__ int swz_v(int r) { return (r >> 1) & 7; }
 // stay <= 256 and O is rescaled rarely.
 constexpr float kRescaleTh = 8.f;
 
+// max / sum of x over both 32-lane halves, for every lane (v_permlane32_swap).
+__device__ __forceinline__ float max_halves(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D, int BLK, bool OUT_F32>
 __global__ __launch_bounds__(BLK * 2, 2) void rr_block_sparse_fa(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ Vt,
@@ -149,47 +161,85 @@ __global__ __launch_bounds__(BLK * 2, 2) void rr_block_sparse_fa(
         return ((unsigned)J <= (unsigned)I) ? J : -1;
     };
 
-    // Start the copies of stage st into (kb, vb); returns false if none.
-    auto issue = [&](int st, char *kb, char *vb) -> bool {
-        const int J = stage_block(st);
+    // Per-lane byte offsets of this wave's copies inside one stage (the same
+    // for every stage): K chunk (row r, slot c^swz) and V^T chunk.  Each copy
+    // is then a uniform per-stage base plus a fixed 32-bit lane offset.
+    uint32_t koff[C::IK], voff[C::IV];
+#pragma unroll
+    for (int i = 0; i < C::IK; ++i) {
+        const int p = (wid * C::IK + i) * 64 + lane;
+        const int r = p / C::CPRK, c = (p % C::CPRK) ^ swz_k<D>(r);
+        koff[i] = (uint32_t)((r * Hkv * D + c * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < C::IV; ++i) {
+        const int p = (wid * C::IV + i) * 64 + lane;
+        const int r = p >> 3, c = (p & 7) ^ swz_v(r);
+        voff[i] = (uint32_t)((r * Lp + c * 8) * 2);
+    }
+    const char *kbase = reinterpret_cast<const char *>(K + (size_t)g * D);
+    const char *vbase = reinterpret_cast<const char *>(Vt + (size_t)g * D * Lp);
+
+    // Start the copies of stage st (key block J) into (kb, vb); returns false
+    // if none.
+    auto issue = [&](int st, int J, char *kb, char *vb) -> bool {
         if (J < 0) return false;
         const int key0 = J * BLK + (st % C::SPB) * C::KT;
+        if (key0 + C::KT <= L) {
+            const char *ks = kbase + (size_t)key0 * Hkv * D * 2;
 #pragma unroll
-        for (int i = 0; i < C::IK; ++i) {
-            const int p = (wid * C::IK + i) * 64 + lane;
-            const int r = p / C::CPRK, sl = p % C::CPRK;
-            const int c = sl ^ swz_k<D>(r);
-            const int key = min(key0 + r, L - 1);
-            g2lds16(K + ((size_t)key * Hkv + g) * D + c * 8, (lds_char *)kb + (wid * C::IK + i) * 1024);
-        }
+            for (int i = 0; i < C::IK; ++i)
+                g2lds16(ks + koff[i], (lds_char *)kb + (wid * C::IK + i) * 1024);
+        } else {
+            // Short last stage: rows past L re-read row L-1 (masked later).
 #pragma unroll
-        for (int i = 0; i < C::IV; ++i) {
-            const int p = (wid * C::IV + i) * 64 + lane;
-            const int r = p >> 3, sl = p & 7;
-            const int c = sl ^ swz_v(r);
-            g2lds16(Vt + ((size_t)g * D + r) * Lp + key0 + c * 8, (lds_char *)vb + (wid * C::IV + i) * 1024);
+            for (int i = 0; i < C::IK; ++i) {
+                const int p = (wid * C::IK + i) * 64 + lane;
+                const int r = p / C::CPRK, c = (p % C::CPRK) ^ swz_k<D>(r);
+                const int key = min(key0 + r, L - 1);
+                g2lds16(K + ((size_t)key * Hkv + g) * D + c * 8, (lds_char *)kb + (wid * C::IK + i) * 1024);
+            }
         }
+        const char *vs = vbase + (size_t)key0 * 2;
+#pragma unroll
+        for (int i = 0; i < C::IV; ++i) g2lds16(vs + voff[i], (lds_char *)vb + (wid * C::IV + i) * 1024);
         return true;
     };
 
-    auto compute = [&](int st, const char *kb, const char *vb) {
-        const int J = stage_block(st);
+    // J is passed in (read before the copies): a scalar load still in flight
+    // here would force every LDS wait below to lgkmcnt(0).
+    auto compute = [&](int st, int J, const char *kb, const char *vb) {
         if (J < 0) return;
         const int key0 = J * BLK + (st % C::SPB) * C::KT;
         const bool diag = (J == I);
         if (diag && I * BLK + wid * 32 + 31 < key0) return;  // whole stage above this wave's rows
 
+        // S^T for both 32-key sub-tiles, d-step by d-step.  K fragments are
+        // read two d-steps ahead of their products; scheduling barriers keep
+        // the compiler from sinking each read next to its consumer, which
+        // would expose one LDS round trip per pair of products.
         f32x16 sacc[2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
-            const char *kr = kb + (kt * 32 + krow) * (D * 2);
+        const char *kr0 = kb + krow * (D * 2);
+        const char *kr1 = kr0 + 32 * (D * 2);
+        uint4 fa[C::NKS], fb[C::NKS];
+        auto rd = [&](int ks) {
+            const int off = ((2 * ks + hk) ^ ksw) << 4;
+            fa[ks] = *reinterpret_cast<const uint4 *>(kr0 + off);
+            fb[ks] = *reinterpret_cast<const uint4 *>(kr1 + off);
+        };
+        rd(0);
+        rd(1);
 #pragma unroll
-            for (int ks = 0; ks < C::NKS; ++ks) {
-                const uint4 a = *reinterpret_cast<const uint4 *>(kr + (((2 * ks + hk) ^ ksw) << 4));
-                sacc[kt] = mfma32x32x16(as_bf16x8(a), qf[ks], sacc[kt]);
-            }
+        for (int ks = 0; ks < C::NKS; ++ks) {
+            if (ks + 2 < C::NKS) rd(ks + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            sacc[0] = mfma32x32x16(as_bf16x8(fa[ks]), qf[ks], sacc[0]);
+            sacc[1] = mfma32x32x16(as_bf16x8(fb[ks]), qf[ks], sacc[1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         float mx = -INFINITY;
@@ -206,8 +256,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void rr_block_sparse_fa(
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
-        mx = fmaxf(mx, xor_lane(mx, 32));
-        const float mxs = mx * scale2;
+        const float mxs = max_halves(mx) * scale2;
         if (__ballot(mxs > m + kRescaleTh) != 0ull) {
             const float mn = fmaxf(m, mxs);
             const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
@@ -247,28 +296,34 @@ __global__ __launch_bounds__(BLK * 2, 2) void rr_block_sparse_fa(
     // Two-stage pipeline over statically distinct LDS buffers: the copies of
     // stage st+1 run while stage st is computed.  Each wave waits for its own
     // copies with vmcnt, the barrier then publishes all waves' copies.
-    if (nst > 0) issue(0, Kb0, Vb0);
+    if (nst > 0) issue(0, stage_block(0), Kb0, Vb0);
     for (int st = 0; st < nst; st += 2) {
-        if (st + 1 < nst && issue(st + 1, Kb1, Vb1))
+        const int J0 = stage_block(st), J1 = st + 1 < nst ? stage_block(st + 1) : -1;
+        const int J2 = st + 2 < nst ? stage_block(st + 2) : -1;
+        // Let these scalar loads land now: scalar results may return out of
+        // order, so one still pending would force every LDS wait in the
+        // compute phase to lgkmcnt(0).
+        wait_lgkm0();
+        if (st + 1 < nst && issue(st + 1, J1, Kb1, Vb1))
             wait_vmcnt<C::LPW>();
         else
             wait_vmcnt<0>();
         bar();
-        compute(st, Kb0, Vb0);
+        compute(st, J0, Kb0, Vb0);
         wait_lgkm0();
         bar();
         if (st + 1 >= nst) break;
-        if (st + 2 < nst && issue(st + 2, Kb0, Vb0))
+        if (st + 2 < nst && issue(st + 2, J2, Kb0, Vb0))
             wait_vmcnt<C::LPW>();
         else
             wait_vmcnt<0>();
         bar();
-        compute(st + 1, Kb1, Vb1);
+        compute(st + 1, J1, Kb1, Vb1);
         wait_lgkm0();
         bar();
     }
 
-    const float tot = lsum + xor_lane(lsum, 32);
+    const float tot = sum_halves(lsum);
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
     if (tq >= L) return;
 #pragma unroll
