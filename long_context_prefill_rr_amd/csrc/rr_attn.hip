@@ -103,7 +103,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 template <int D, int BLK, bool OUT_F32>
 __global__ __launch_bounds__(BLK * 2, 2) void rr_block_sparse_fa(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ Vt,
-    int L, int Lp, int Hq, int Hkv, int nb, int nq, const int32_t *__restrict__ counts,
+    int L, int Lp, int Hq, int Hkv, int nb, int nq, int chunk, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ block_idx, void *__restrict__ O, float scale2) {
     using C = FaCfg<D, BLK>;
     __shared__ __attribute__((aligned(1024))) char Kb0[C::KBYTES];
@@ -112,12 +112,19 @@ __global__ __launch_bounds__(BLK * 2, 2) void rr_block_sparse_fa(
     __shared__ __attribute__((aligned(1024))) char Vb1[C::VBYTES];
 
     const int G = Hq / Hkv;
-    // Work decode: groups (kv-head g, block-row I) in kv-head-major order with
-    // I descending; the G query heads of a group are consecutive on one XCD.
+    // Work decode: groups qi = (kv-head g, block-row I) in kv-head-major order
+    // with I descending.  Work-groups are dealt to the 8 XCDs round-robin, so
+    // XCD x runs bx = x, x+8, ...; its slot-th work-group gets group
+    // qi = (c*8 + x)*chunk + j and head hh, with (c, j, hh) = slot in mixed
+    // radix (., chunk, G).  Each XCD thus holds `chunk` consecutive block-rows
+    // of one kv-head (all G heads) at a time: their kept lists overlap (shared
+    // sinks, verticals, neighbouring local blocks) and are walked in the same
+    // ascending order, so the K/V tiles they share come from its L2.
     const int bx = blockIdx.x;
     const int x = bx & 7, slot = bx >> 3;
     const int hh = slot % G;
-    const int qi = (slot / G) * 8 + x;
+    const int jj = (slot / G) % chunk;
+    const int qi = ((slot / (G * chunk)) * 8 + x) * chunk + jj;
     if (qi >= nq) return;
     const int g = qi / nb;
     const int I = nb - 1 - qi % nb;
@@ -355,17 +362,22 @@ template <int D, int BLK>
 static void launch_fa_t(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, const Shape &s,
                         const int32_t *counts, const int32_t *block_idx, void *O, bool out_f32,
                         hipStream_t st) {
+#ifndef RR_FA_CHUNK
+#define RR_FA_CHUNK 1
+#endif
+    const int chunk = RR_FA_CHUNK;  // consecutive block-rows per XCD at a time
     const int nq = s.nb * s.Hkv;
-    const int nq8 = (nq + 7) / 8 * 8;
-    const dim3 grid((unsigned)(nq8 * s.G));
+    const int per = 8 * chunk;
+    const int nqp = (nq + per - 1) / per * per;
+    const dim3 grid((unsigned)(nqp * s.G));
     const float scale2 = kLog2e / sqrtf((float)D);
     const int Lp = s.nb * BLK;
     if (out_f32)
         hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true>), grid, dim3(BLK * 2), 0, st, Q, K, Vt,
-                           s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O, scale2);
+                           s.L, Lp, s.Hq, s.Hkv, s.nb, nq, chunk, counts, block_idx, O, scale2);
     else
         hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false>), grid, dim3(BLK * 2), 0, st, Q, K,
-                           Vt, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O, scale2);
+                           Vt, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, chunk, counts, block_idx, O, scale2);
 }
 
 hipError_t launch_block_sparse_fa(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt,
