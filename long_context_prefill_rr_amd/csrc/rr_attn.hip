@@ -57,10 +57,13 @@ __global__ __launch_bounds__(256) void rr_transpose_v(const uint16_t *__restrict
     }
 }
 
-// Tile constants of the attention kernel: 64-key stages, BLK/32 waves.
+// Tile constants of the attention kernel.  A work-group holds two head
+// groups of BLK/32 waves (two query heads that share one kv-head); each wave
+// owns one 32-row query tile.  Keys are walked in 64-key stages.
 template <int D, int BLK>
 struct FaCfg {
-    static constexpr int NW = BLK / 32;                 // waves (32 query rows each)
+    static constexpr int NWG = BLK / 32;                // waves per head group
+    static constexpr int NW = 2 * NWG;                  // waves per work-group
     static constexpr int NT = NW * 64;                  // threads
     static constexpr int KT = 64;                       // keys per pipeline stage
     static constexpr int SPB = BLK / KT;                // stages per key block
@@ -72,6 +75,7 @@ struct FaCfg {
     static constexpr int VBYTES = D * KT * 2;
     static constexpr int NDT = D / 32;
     static constexpr int NKS = D / 16;
+    static constexpr int MAXNB = 4096;                  // longest block list
 };
 
 // LDS swizzles (16-byte slot XOR per row) chosen so that the 16 rows read by
@@ -101,39 +105,94 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 template <int D, int BLK, bool OUT_F32>
-__global__ __launch_bounds__(BLK * 2, 2) void rr_block_sparse_fa(
+__global__ __launch_bounds__(BLK * 4, 2) void rr_block_sparse_fa(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ Vt,
-    int L, int Lp, int Hq, int Hkv, int nb, int nq, int chunk, const int32_t *__restrict__ counts,
+    int L, int Lp, int Hq, int Hkv, int nb, int nq, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ block_idx, void *__restrict__ O, float scale2) {
     using C = FaCfg<D, BLK>;
     __shared__ __attribute__((aligned(1024))) char Kb0[C::KBYTES];
     __shared__ __attribute__((aligned(1024))) char Kb1[C::KBYTES];
     __shared__ __attribute__((aligned(1024))) char Vb0[C::VBYTES];
     __shared__ __attribute__((aligned(1024))) char Vb1[C::VBYTES];
+    __shared__ uint32_t ulist[C::MAXNB];          // union of the two kept lists
+    __shared__ uint32_t bits[2][C::MAXNB / 32];   // per-head membership bitmaps
+    __shared__ int scan_part[C::NW];
+    __shared__ int nunion;
 
     const int G = Hq / Hkv;
-    // Work decode: groups qi = (kv-head g, block-row I) in kv-head-major order
-    // with I descending.  Work-groups are dealt to the 8 XCDs round-robin, so
-    // XCD x runs bx = x, x+8, ...; its slot-th work-group gets group
-    // qi = (c*8 + x)*chunk + j and head hh, with (c, j, hh) = slot in mixed
-    // radix (., chunk, G).  Each XCD thus holds `chunk` consecutive block-rows
-    // of one kv-head (all G heads) at a time: their kept lists overlap (shared
-    // sinks, verticals, neighbouring local blocks) and are walked in the same
-    // ascending order, so the K/V tiles they share come from its L2.
+    const int npair = (G + 1) >> 1;
+    // Work decode: (kv-head g, block-row I) pairs qi in kv-head-major order
+    // with I descending, times head pairs.  Work-groups are dealt to the 8
+    // XCDs round-robin, so XCD x runs bx = x, x+8, ...: its slot-th work-group
+    // gets pair qi = (slot / npair)*8 + x and head pair slot % npair.  The 8
+    // XCDs work on neighbouring block-rows of one kv-head at a time (their
+    // K/V tiles meet in the shared last-level cache) and the head pairs of
+    // one row stay on one XCD (sharing its L2).
     const int bx = blockIdx.x;
     const int x = bx & 7, slot = bx >> 3;
-    const int hh = slot % G;
-    const int jj = (slot / G) % chunk;
-    const int qi = ((slot / (G * chunk)) * 8 + x) * chunk + jj;
+    const int pp = slot % npair;
+    const int qi = (slot / npair) * 8 + x;
     if (qi >= nq) return;
     const int g = qi / nb;
     const int I = nb - 1 - qi % nb;
-    const int h = g * G + hh;
 
     const int tid = threadIdx.x;
     const int wid = tid >> 6, lane = tid & 63;
+    const int gr = wid / C::NWG;              // head group of this wave
+    const int rw = wid % C::NWG;              // 32-row tile of this wave
     const int col = lane & 31, hk = lane >> 5;
-    const int tq = I * BLK + wid * 32 + col;
+    const bool head_ok = 2 * pp + gr < G;     // odd G: the last pair has one head
+    const int h = g * G + min(2 * pp + gr, G - 1);
+    const int tq = I * BLK + rw * 32 + col;
+    const int wave_last_row = I * BLK + rw * 32 + 31;
+
+    // Union of the two heads' kept lists (ascending key blocks, each tagged
+    // with the heads that keep it), built in LDS: membership bitmaps, then a
+    // work-group scan compacts the set blocks in index order.
+    const int nbw = (nb + 31) >> 5;
+    for (int i = tid; i < 2 * (C::MAXNB / 32); i += C::NT) (&bits[0][0])[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        if (2 * pp + q >= G) continue;
+        const int hq = g * G + 2 * pp + q;
+        const int cq = min(max(counts[(size_t)hq * nb + I], 0), nb);
+        const int32_t *lq = block_idx + ((size_t)hq * nb + I) * nb;
+        for (int k = tid; k < cq; k += C::NT) {
+            const int J = lq[k];
+            if ((unsigned)J <= (unsigned)I) atomicOr(&bits[q][J >> 5], 1u << (J & 31));
+        }
+    }
+    __syncthreads();
+    {
+        const int E = (nb + C::NT - 1) / C::NT;
+        const int j0 = tid * E;
+        int cnt_local = 0;
+        for (int e = 0; e < E; ++e) {
+            const int J = j0 + e;
+            if (J < nb && ((bits[0][J >> 5] | bits[1][J >> 5]) >> (J & 31)) & 1u) ++cnt_local;
+        }
+        int incl = cnt_local;
+#pragma unroll
+        for (int o2 = 1; o2 < 64; o2 <<= 1) {
+            const int t = __shfl_up(incl, o2, 64);
+            if (lane >= o2) incl += t;
+        }
+        if (lane == 63) scan_part[wid] = incl;
+        __syncthreads();
+        int pre = 0;
+        for (int w = 0; w < wid; ++w) pre += scan_part[w];
+        int pos = pre + incl - cnt_local;
+        for (int e = 0; e < E; ++e) {
+            const int J = j0 + e;
+            if (J >= nb) break;
+            const uint32_t b0 = (bits[0][J >> 5] >> (J & 31)) & 1u, b1 = (bits[1][J >> 5] >> (J & 31)) & 1u;
+            if (b0 | b1) ulist[pos++] = (uint32_t)J | (b0 << 16) | (b1 << 17);
+        }
+        if (tid == C::NT - 1) nunion = pre + incl;
+        __syncthreads();
+    }
+    (void)nbw;
 
     bf16x8 qf[C::NKS];
     {
@@ -155,17 +214,13 @@ __global__ __launch_bounds__(BLK * 2, 2) void rr_block_sparse_fa(
     const int ksw = swz_k<D>(krow);
     const int vsw = swz_v(col);
 
-    const int cnt = min(max(counts[(size_t)h * nb + I], 0), nb);
-    const int32_t *lst = block_idx + ((size_t)h * nb + I) * nb;
-    const int nst = cnt * C::SPB;
+    const int nst = nunion * C::SPB;
 
-    // Key block of stage st, -1 for an out-of-range list entry (skipped).
-    // The index is made provably uniform so the entry comes through a scalar
-    // load: a vector load would share vmcnt with the LDS copies in flight.
-    auto stage_block = [&](int st) -> int {
-        const int it = __builtin_amdgcn_readfirstlane(st / C::SPB);
-        const int J = lst[it];
-        return ((unsigned)J <= (unsigned)I) ? J : -1;
+    // Union entry of stage st: key block in the low 16 bits, bit 16+q set
+    // when head q of the pair keeps it.  Read from LDS, made wave-uniform.
+    auto stage_entry = [&](int st) -> int {
+        if (st >= nst) return -1;
+        return __builtin_amdgcn_readfirstlane((int)ulist[st / C::SPB]);
     };
 
     // Per-lane byte offsets of this wave's copies inside one stage (the same
@@ -189,8 +244,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void rr_block_sparse_fa(
 
     // Start the copies of stage st (key block J) into (kb, vb); returns false
     // if none.
-    auto issue = [&](int st, int J, char *kb, char *vb) -> bool {
-        if (J < 0) return false;
+    auto issue = [&](int st, int ent, char *kb, char *vb) -> bool {
+        if (ent < 0) return false;
+        const int J = ent & 0xffff;
         const int key0 = J * BLK + (st % C::SPB) * C::KT;
         if (key0 + C::KT <= L) {
             const char *ks = kbase + (size_t)key0 * Hkv * D * 2;
@@ -213,13 +269,14 @@ __global__ __launch_bounds__(BLK * 2, 2) void rr_block_sparse_fa(
         return true;
     };
 
-    // J is passed in (read before the copies): a scalar load still in flight
-    // here would force every LDS wait below to lgkmcnt(0).
-    auto compute = [&](int st, int J, const char *kb, const char *vb) {
-        if (J < 0) return;
+    // The entry is passed in (read at the top of the iteration, before the
+    // copies), so no LDS read of the list is pending during the products.
+    auto compute = [&](int st, int ent, const char *kb, const char *vb) {
+        if (ent < 0 || !((ent >> (16 + gr)) & 1)) return;  // not kept by this wave's head
+        const int J = ent & 0xffff;
         const int key0 = J * BLK + (st % C::SPB) * C::KT;
         const bool diag = (J == I);
-        if (diag && I * BLK + wid * 32 + 31 < key0) return;  // whole stage above this wave's rows
+        if (diag && wave_last_row < key0) return;  // whole stage above this wave's rows
 
         // S^T for both 32-key sub-tiles, d-step by d-step.  K fragments are
         // read two d-steps ahead of their products; scheduling barriers keep
@@ -303,36 +360,31 @@ __global__ __launch_bounds__(BLK * 2, 2) void rr_block_sparse_fa(
     // Two-stage pipeline over statically distinct LDS buffers: the copies of
     // stage st+1 run while stage st is computed.  Each wave waits for its own
     // copies with vmcnt, the barrier then publishes all waves' copies.
-    if (nst > 0) issue(0, stage_block(0), Kb0, Vb0);
+    if (nst > 0) issue(0, stage_entry(0), Kb0, Vb0);
     for (int st = 0; st < nst; st += 2) {
-        const int J0 = stage_block(st), J1 = st + 1 < nst ? stage_block(st + 1) : -1;
-        const int J2 = st + 2 < nst ? stage_block(st + 2) : -1;
-        // Let these scalar loads land now: scalar results may return out of
-        // order, so one still pending would force every LDS wait in the
-        // compute phase to lgkmcnt(0).
-        wait_lgkm0();
-        if (st + 1 < nst && issue(st + 1, J1, Kb1, Vb1))
+        const int E0 = stage_entry(st), E1 = stage_entry(st + 1), E2 = stage_entry(st + 2);
+        if (st + 1 < nst && issue(st + 1, E1, Kb1, Vb1))
             wait_vmcnt<C::LPW>();
         else
             wait_vmcnt<0>();
         bar();
-        compute(st, J0, Kb0, Vb0);
+        compute(st, E0, Kb0, Vb0);
         wait_lgkm0();
         bar();
         if (st + 1 >= nst) break;
-        if (st + 2 < nst && issue(st + 2, J2, Kb0, Vb0))
+        if (st + 2 < nst && issue(st + 2, E2, Kb0, Vb0))
             wait_vmcnt<C::LPW>();
         else
             wait_vmcnt<0>();
         bar();
-        compute(st + 1, J1, Kb1, Vb1);
+        compute(st + 1, E1, Kb1, Vb1);
         wait_lgkm0();
         bar();
     }
 
     const float tot = sum_halves(lsum);
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
-    if (tq >= L) return;
+    if (tq >= L || !head_ok) return;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) {
 #pragma unroll
@@ -362,22 +414,17 @@ template <int D, int BLK>
 static void launch_fa_t(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, const Shape &s,
                         const int32_t *counts, const int32_t *block_idx, void *O, bool out_f32,
                         hipStream_t st) {
-#ifndef RR_FA_CHUNK
-#define RR_FA_CHUNK 1
-#endif
-    const int chunk = RR_FA_CHUNK;  // consecutive block-rows per XCD at a time
     const int nq = s.nb * s.Hkv;
-    const int per = 8 * chunk;
-    const int nqp = (nq + per - 1) / per * per;
-    const dim3 grid((unsigned)(nqp * s.G));
+    const int nq8 = (nq + 7) / 8 * 8;
+    const dim3 grid((unsigned)(nq8 * ((s.G + 1) / 2)));
     const float scale2 = kLog2e / sqrtf((float)D);
     const int Lp = s.nb * BLK;
     if (out_f32)
-        hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true>), grid, dim3(BLK * 2), 0, st, Q, K, Vt,
-                           s.L, Lp, s.Hq, s.Hkv, s.nb, nq, chunk, counts, block_idx, O, scale2);
+        hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true>), grid, dim3(BLK * 4), 0, st, Q, K, Vt,
+                           s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O, scale2);
     else
-        hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false>), grid, dim3(BLK * 2), 0, st, Q, K,
-                           Vt, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, chunk, counts, block_idx, O, scale2);
+        hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false>), grid, dim3(BLK * 4), 0, st, Q, K,
+                           Vt, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O, scale2);
 }
 
 hipError_t launch_block_sparse_fa(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt,
