@@ -84,6 +84,29 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (
 // orders LDS traffic with explicit waits.
 __device__ __forceinline__ void bar() { __builtin_amdgcn_s_barrier(); }
 
+// op(x[lane], x[lane ^ 16]) and op(x[lane], x[lane ^ 32]) for every lane
+// through v_permlane16_swap / v_permlane32_swap (no LDS round trip).
+__device__ __forceinline__ float xor16_max(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Merge two (max, sum-of-2^(x-max)) pairs.  (-inf, 0) is the identity.
 __device__ __forceinline__ void merge_max_sum(float &m, float &z, float m2, float z2) {
     float nm = fmaxf(m, m2);

@@ -15,6 +15,8 @@
 // hi + mid + lo bf16 planes (24 significand bits) and each plane is a
 // separate MFMA pass with fp32 accumulation.  Scores live in the log2 domain
 // (scaled by log2(e)/sqrt(d)) so exponentials are single v_exp_f32.
+#include <algorithm>
+
 #include "rr_device.h"
 #include "rr_internal.h"
 
@@ -75,198 +77,246 @@ __device__ __forceinline__ long long packed_row_offset(int C, int I, int a) {
 }
 
 // ---------------------------------------------------------------------------
-// rr_score: one work-group per (query block-row I, kv-head g, chunk of 64
-// sampled rows).  The rows are the (query head, stride) pairs of the G heads
-// that share kv-head g, for the C strides of block I: row (hh, a) samples
-// token (I*C + a)*S + ((g*G + hh) mod S).  Four waves split the key strides
-// 0 .. (I+1)*C-1 into groups of max(C, 16) and each wave computes, for all 64
-// rows, S^T = Kbar . Q^T tiles of 16 strides x 16 rows on
-// v_mfma_f32_16x16x32_bf16 (3 planes x d/32 steps).  For every (row,
-// key-block) it keeps max and sum of 2^(s - max) over the block's strides
-// j <= i and writes them; per-row totals are merged across waves into
+// rr_score: one work-group per (group of R consecutive query block-rows
+// I0 .. I0+R-1, kv-head g, chunk of up to 256 sampled rows).  The rows are
+// the (block-row, query head, stride) triples of the G heads that share
+// kv-head g: row (I, hh, a) samples token (I*C + a)*S + ((g*G + hh) mod S).
+// R is chosen so that a work-group holds about 256 rows: every pooled-key
+// fragment streamed from memory then feeds 16 row tiles, which keeps the
+// vector-memory path (the bound of a 64-row design) well below the matrix
+// unit's rate.  The rows' Q tile sits in LDS (XOR-swizzled 16-byte slots).
+// Each wave computes S^T = Kbar . Q^T tiles of 16 strides x 16 rows on
+// v_mfma_f32_16x16x32_bf16 (3 planes x d/32 steps) for all rows; the waves
+// split the key strides 0 .. (I0+R)*C-1 into units of 16 strides
+// (C >= 16: whole blocks J = wave, wave+4, ...; C < 16: 16-stride units).
+// Fragments of the unit after next are loaded while a unit is processed.
+// For every (row, key-block) it writes max and sum of 2^(s - max) over the
+// block's strides j <= i; per-row totals are merged across waves into
 // rowstat.  Nothing of the [rows x strides] score matrix reaches memory.
 // ---------------------------------------------------------------------------
+constexpr int kScoreRows = 256;
+
 template <int D, int C>
 __global__ __launch_bounds__(256) void rr_score(const uint16_t *__restrict__ Q,
                                                 const uint16_t *__restrict__ Kp, int Hq, int Hkv,
-                                                int S, int nb, int ns, int G, int nchunks,
+                                                int S, int nb, int ns, int G, int R, int nchunks,
                                                 long long P, float scale2,
                                                 float2 *__restrict__ stats,
                                                 float2 *__restrict__ rowstat) {
     constexpr int KS = D / 32;
-    constexpr int KG = C >= 16 ? C : 16;
-    constexpr int NSUB = KG / 16;
+    constexpr int CPR = D / 8;                 // 16-byte chunks per Q row
+    constexpr int NSUB = C >= 16 ? C / 16 : 1;
+    constexpr int MT = kScoreRows / 16;        // row tiles per work-group
+    __shared__ __attribute__((aligned(16))) uint16_t qs[kScoreRows * D];
+    __shared__ float2 red[4][kScoreRows];
+
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lr = lane & 15, lg = lane >> 4;
 
+    // Decode: block-row groups in descending order (long rows first).
     int b = blockIdx.x;
     const int chunk = b % nchunks;
     b /= nchunks;
     const int g = b % Hkv;
-    const int I = nb - 1 - b / Hkv;
-    const int cI = min(C, ns - I * C);
+    const int ngrp = (nb + R - 1) / R;
+    const int I0 = (ngrp - 1 - b / Hkv) * R;
+    const int GC = G * C;
+    const int rows_total = min(R, nb - I0) * GC;           // rows of this block-row group
+    const int row0 = chunk * kScoreRows;
+    const int rows_here = min(kScoreRows, rows_total - row0);
+    const int NT = (rows_here + 15) >> 4;
+    const int Itop = min(I0 + R, nb) - 1;                   // last block-row of the group
     const size_t plane = (size_t)Hkv * ns * D;
     const uint16_t *kb = Kp + (size_t)g * ns * D;
-    const int rows_here = min(64, G * C - chunk * 64);
-    const int NT = (rows_here + 15) >> 4;
 
-    bf16x8 qf[4][KS];
-    int row_i[4], row_h[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const int f = chunk * 64 + rt * 16 + lr;
-        const int hh = f / C, a = f % C;
-        const bool valid = (rt < NT) && hh < G && a < cI;
-        row_i[rt] = valid ? I * C + a : -1;
-        row_h[rt] = g * G + (hh < G ? hh : 0);
-        const int t = valid ? row_i[rt] * S + (row_h[rt] % S) : 0;
-        const uint16_t *qp = Q + ((size_t)t * Hq + row_h[rt]) * D + lg * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qf[rt][ks] = valid ? as_bf16x8(ld16(qp + ks * 32)) : as_bf16x8(zero_u4());
+    // Row f (0..rows_here) -> (block-row, head, stride); -1 stride if invalid.
+    auto row_of = [&](int f, int &I, int &h, int &i) {
+        const int ff = row0 + f;
+        I = I0 + ff / GC;
+        const int rem = ff % GC, hh = rem / C, a = rem % C;
+        h = g * G + hh;
+        const int cI = min(C, ns - I * C);
+        i = (f < rows_here && a < cI) ? I * C + a : -1;
+    };
+
+    // Stage the Q rows in LDS: chunk c of row f at slot c ^ (f & 15).
+    for (int idx = threadIdx.x; idx < kScoreRows * CPR; idx += 256) {
+        const int f = idx / CPR, c = idx % CPR;
+        int I, h, i;
+        row_of(f, I, h, i);
+        uint4 v = zero_u4();
+        if (i >= 0) {
+            const int t = i * S + (h % S);
+            v = ld16(Q + ((size_t)t * Hq + h) * D + c * 8);
+        }
+        st16(&qs[f * D + ((c ^ (f & 15)) & (CPR - 1)) * 8], v);
     }
 
-    float rM[4], rZ[4];
+    // This lane's row in each tile (column of the S^T tiles).
+    int row_i[MT], row_h[MT];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    for (int rt = 0; rt < MT; ++rt) {
+        int I, h, i;
+        row_of(rt * 16 + lr, I, h, i);
+        row_i[rt] = (rt < NT) ? i : -1;
+        row_h[rt] = h;
+    }
+    __syncthreads();
+
+    float rM[MT], rZ[MT];
+#pragma unroll
+    for (int rt = 0; rt < MT; ++rt) {
         rM[rt] = -INFINITY;
         rZ[rt] = 0.f;
     }
 
-    const int nkeys = (I + 1) * C;
-    const int ngroups = (nkeys + KG - 1) / KG;
-    for (int u = wid; u < ngroups; u += 4) {
-        if constexpr (C >= 16) {
-            const int J = u;
-            float bm[4], bz[4];
+    // Units of this wave (16 strides each) over the strides of blocks 0..Itop.
+    const int nkeys = (Itop + 1) * C;
+    int nunits;
+    if constexpr (C >= 16) {
+        const int nblk = (Itop >= wid) ? (Itop - wid) / 4 + 1 : 0;
+        nunits = nblk * NSUB;
+    } else {
+        const int ng = (nkeys + 15) / 16;
+        nunits = (ng > wid) ? (ng - 1 - wid) / 4 + 1 : 0;
+    }
+    auto unit_j0 = [&](int t) -> int {
+        if constexpr (C >= 16)
+            return (wid + 4 * (t / NSUB)) * C + (t % NSUB) * 16;
+        else
+            return (wid + 4 * t) * 16;
+    };
+    auto load = [&](int t, bf16x8 (&ka)[3][KS]) {
+        const int jr = min(unit_j0(t) + lr, ns - 1);
+        const uint16_t *src = kb + (size_t)jr * D + lg * 8;
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                bm[rt] = -INFINITY;
-                bz[rt] = 0.f;
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) ka[p][ks] = as_bf16x8(ld16(src + p * plane + ks * 32));
+    };
+
+    float bm[MT], bz[MT];  // running block statistics when a block spans units
+#pragma unroll
+    for (int rt = 0; rt < MT; ++rt) {
+        bm[rt] = -INFINITY;
+        bz[rt] = 0.f;
+    }
+
+    auto write_stat = [&](int rt, int J, float m, float z) {
+        if (lg == 0 && row_i[rt] >= 0 && J * C <= row_i[rt] && m != -INFINITY) {
+            const int I = row_i[rt] / C, a = row_i[rt] - I * C;
+            stats[(size_t)row_h[rt] * P + packed_row_offset(C, I, a) + J] = make_float2(m, z);
+            merge_max_sum(rM[rt], rZ[rt], m, z);
+        }
+    };
+
+    auto process = [&](int t, bf16x8 (&ka)[3][KS]) {
+        const int j0 = unit_j0(t);
+        // Causal masking only where a unit reaches the first stride of block I0.
+        const bool diag = j0 + 15 >= I0 * C;
+#pragma unroll
+        for (int rt = 0; rt < MT; ++rt) {
+            if (rt >= NT) break;
+            const int f = rt * 16 + lr;
+            const uint16_t *qrow = &qs[f * D];
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int c = ks * 4 + lg;
+                const bf16x8 qb = as_bf16x8(ld16(qrow + ((c ^ (f & 15)) & (CPR - 1)) * 8));
+#pragma unroll
+                for (int p = 0; p < 3; ++p) acc = mfma16x16x32(ka[p][ks], qb, acc);
             }
-            for (int sub = 0; sub < NSUB; ++sub) {
-                const int j0 = J * C + sub * 16;
-                const int jr = min(j0 + lr, ns - 1);
-                bf16x8 ka[3][KS];
+            if (diag) {
 #pragma unroll
-                for (int p = 0; p < 3; ++p)
+                for (int e = 0; e < 4; ++e)
+                    if (j0 + lg * 4 + e > row_i[rt]) acc[e] = -INFINITY;
+            }
+            if constexpr (C >= 16) {
+                const int J = j0 / C;
+                const int sub = (j0 % C) / 16;
+                float mr = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+                mr = xor16_max(mr);
+                mr = xor32_max(mr);
+                const float m = mr * scale2;
+                float z = 0.f;
+                if (mr != -INFINITY) {
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        ka[p][ks] = as_bf16x8(ld16(kb + p * plane + (size_t)jr * D + ks * 32 + lg * 8));
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    if (rt >= NT) break;
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int p = 0; p < 3; ++p)
-#pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(ka[p][ks], qf[rt][ks], acc);
-                    float s[4], tm = -INFINITY;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int j = j0 + lg * 4 + e;
-                        s[e] = (j <= row_i[rt]) ? acc[e] * scale2 : -INFINITY;
-                        tm = fmaxf(tm, s[e]);
+                    for (int e = 0; e < 4; ++e) z += fast_exp2(fmaf(acc[e], scale2, -m));
+                }
+                z = xor16_sum(z);
+                z = xor32_sum(z);
+                if constexpr (NSUB == 1) {
+                    write_stat(rt, J, m, z);
+                } else {
+                    merge_max_sum(bm[rt], bz[rt], m, z);
+                    if (sub == NSUB - 1) {
+                        write_stat(rt, J, bm[rt], bz[rt]);
+                        bm[rt] = -INFINITY;
+                        bz[rt] = 0.f;
                     }
-                    tm = fmaxf(tm, xor_lane(tm, 16));
-                    tm = fmaxf(tm, xor_lane(tm, 32));
-                    const float nm = fmaxf(bm[rt], tm);
-                    if (nm != -INFINITY) {
-                        float z = (bm[rt] == -INFINITY) ? 0.f : bz[rt] * fast_exp2(bm[rt] - nm);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (s[e] != -INFINITY) z += fast_exp2(s[e] - nm);
-                        bz[rt] = z;
-                        bm[rt] = nm;
-                    }
                 }
-            }
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                if (rt >= NT) break;
-                float z = bz[rt];
-                z += xor_lane(z, 16);
-                z += xor_lane(z, 32);
-                if (lg == 0 && row_i[rt] >= 0) {
-                    const int a = row_i[rt] - I * C;
-                    stats[(size_t)row_h[rt] * P + packed_row_offset(C, I, a) + J] = make_float2(bm[rt], z);
-                    merge_max_sum(rM[rt], rZ[rt], bm[rt], z);
-                }
-            }
-        } else {
-            constexpr int KPB = C < 4 ? C : 4;  // keys of one block held by a lane
-            constexpr int BPL = 4 / KPB;        // blocks per lane
-            const int j0 = u * 16;
-            const int jr = min(j0 + lr, ns - 1);
-            bf16x8 ka[3][KS];
-#pragma unroll
-            for (int p = 0; p < 3; ++p)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    ka[p][ks] = as_bf16x8(ld16(kb + p * plane + (size_t)jr * D + ks * 32 + lg * 8));
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                if (rt >= NT) break;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int p = 0; p < 3; ++p)
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(ka[p][ks], qf[rt][ks], acc);
-                float s[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = j0 + lg * 4 + e;
-                    s[e] = (j <= row_i[rt]) ? acc[e] * scale2 : -INFINITY;
-                }
+            } else {
+                constexpr int KPB = C < 4 ? C : 4;  // keys of one block held by a lane
+                constexpr int BPL = 4 / KPB;        // blocks per lane
 #pragma unroll
                 for (int bi = 0; bi < BPL; ++bi) {
-                    float m = -INFINITY;
+                    float mr = -INFINITY;
 #pragma unroll
-                    for (int e = bi * KPB; e < (bi + 1) * KPB; ++e) m = fmaxf(m, s[e]);
-                    if constexpr (C == 8) m = fmaxf(m, xor_lane(m, 16));
+                    for (int e = bi * KPB; e < (bi + 1) * KPB; ++e) mr = fmaxf(mr, acc[e]);
+                    if constexpr (C == 8) mr = xor16_max(mr);
+                    const float m = mr * scale2;
                     float z = 0.f;
-                    if (m != -INFINITY) {
+                    if (mr != -INFINITY) {
 #pragma unroll
-                        for (int e = bi * KPB; e < (bi + 1) * KPB; ++e)
-                            if (s[e] != -INFINITY) z += fast_exp2(s[e] - m);
+                        for (int e = bi * KPB; e < (bi + 1) * KPB; ++e) z += fast_exp2(fmaf(acc[e], scale2, -m));
                     }
-                    if constexpr (C == 8) z += xor_lane(z, 16);
+                    if constexpr (C == 8) z = xor16_sum(z);
                     const int J = (j0 + lg * 4 + bi * KPB) / C;
                     const bool writer = (C == 8) ? ((lg & 1) == 0) : true;
-                    if (writer && row_i[rt] >= 0 && m != -INFINITY) {
-                        const int a = row_i[rt] - I * C;
+                    if (writer && row_i[rt] >= 0 && mr != -INFINITY) {
+                        const int I = row_i[rt] / C, a = row_i[rt] - I * C;
                         stats[(size_t)row_h[rt] * P + packed_row_offset(C, I, a) + J] = make_float2(m, z);
                         merge_max_sum(rM[rt], rZ[rt], m, z);
                     }
                 }
             }
         }
+        // The fragments are consumed: refill them with the unit after next.
+        if (t + 2 < nunits) load(t + 2, ka);
+    };
+
+    bf16x8 kA[3][KS], kB[3][KS];
+    if (nunits > 0) load(0, kA);
+    if (nunits > 1) load(1, kB);
+    for (int t = 0; t < nunits; t += 2) {
+        process(t, kA);
+        if (t + 1 >= nunits) break;
+        process(t + 1, kB);
     }
 
     // Per-row totals: butterfly over the four lane groups, then across waves.
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    for (int rt = 0; rt < MT; ++rt) {
         float m2 = xor_lane(rM[rt], 16), z2 = xor_lane(rZ[rt], 16);
         merge_max_sum(rM[rt], rZ[rt], m2, z2);
         m2 = xor_lane(rM[rt], 32);
         z2 = xor_lane(rZ[rt], 32);
         merge_max_sum(rM[rt], rZ[rt], m2, z2);
     }
-    __shared__ float2 red[4][64];
     if (lg == 0) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) red[wid][rt * 16 + lr] = make_float2(rM[rt], rZ[rt]);
+        for (int rt = 0; rt < MT; ++rt) red[wid][rt * 16 + lr] = make_float2(rM[rt], rZ[rt]);
     }
     __syncthreads();
-    if (threadIdx.x < 64) {
-        const int r = threadIdx.x;
+    {
+        const int r = threadIdx.x;  // kScoreRows == 256 threads
         float M = -INFINITY, Z = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) merge_max_sum(M, Z, red[w][r].x, red[w][r].y);
-        const int f = chunk * 64 + r;
-        const int hh = f / C, a = f % C;
-        if (r < rows_here && hh < G && a < cI)
-            rowstat[(size_t)(g * G + hh) * ns + I * C + a] = make_float2(M, Z);
+        int I, h, i;
+        row_of(r, I, h, i);
+        if (i >= 0) rowstat[(size_t)h * ns + i] = make_float2(M, Z);
     }
 }
 
@@ -320,13 +370,16 @@ hipError_t launch_pool_k(const uint16_t *K, const Shape &s, uint16_t *kplanes, h
 
 template <int D>
 static void launch_score_d(const uint16_t *Q, const Shape &s, const EstimateWs &w, hipStream_t st) {
-    const int nchunks = (s.G * s.c + 63) / 64;
-    const dim3 grid((unsigned)(s.nb * s.Hkv * nchunks));
+    const int GC = s.G * s.c;
+    const int R = std::max(1, std::min(s.nb, kScoreRows / GC));  // block-rows per work-group
+    const int nchunks = (R * GC + kScoreRows - 1) / kScoreRows;
+    const int ngrp = (s.nb + R - 1) / R;
+    const dim3 grid((unsigned)(ngrp * s.Hkv * nchunks));
     const float scale2 = kLog2e / sqrtf((float)D);
 #define RR_SCORE_CASE(CC)                                                                      \
     case CC:                                                                                   \
         hipLaunchKernelGGL((rr_score<D, CC>), grid, dim3(256), 0, st, Q, w.kplanes, s.Hq, s.Hkv, \
-                           s.S, s.nb, s.ns, s.G, nchunks, s.P, scale2, w.stats, w.rowstat);    \
+                           s.S, s.nb, s.ns, s.G, R, nchunks, s.P, scale2, w.stats, w.rowstat); \
         break;
     switch (s.c) {
         RR_SCORE_CASE(1)
