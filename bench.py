@@ -35,6 +35,36 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 
 
+CSRC = os.path.join(ROOT, "long_context_prefill_rr_amd", "csrc")
+ATTN_TRAFFIC = (os.path.join(ROOT, "profiles", "rr_block_sparse_fa_llama8b-128k_traffic.md"),
+                ["rr_attn.hip"])
+EST_TRAFFIC = (os.path.join(ROOT, "profiles", "rr_estimate_select_llama8b-128k_traffic.md"),
+               ["rr_estimate.hip", "rr_select.hip"])
+
+
+def measured_traffic(workload_name, spec, field):
+    """Bytes per launch from a committed FETCH_SIZE / WRITE_SIZE summary, if it
+    was taken on the current kernel sources and on this workload; else None."""
+    import hashlib
+    path, sources = spec
+    if workload_name != "llama8b-128k" or not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != h.hexdigest():
+        return None
+    try:
+        return float(fields[field])
+    except (KeyError, ValueError):
+        return None
+
+
 def log(msg):
     sys.stderr.write("[bench] %s\n" % msg)
     sys.stderr.flush()
@@ -59,7 +89,7 @@ def kept_block_flops(counts, idx, L, B, d):
     return float(4.0 * d * pairs.sum().item()), int(valid.sum().item()), int(diag.sum().item())
 
 
-def cpu_baseline(w, g, kept_pairs_all, dense_flops, budget_rows):
+def cpu_baseline(w, g, kept_pairs_all, dense_flops, budget_rows, tokens_per_row=16):
     """Time the fp64 oracle on a sample of block-rows and scale to the workload."""
     import oracle
     nb, B, S, Hq = w.nb, w.B, w.S, w.Hq
@@ -83,7 +113,7 @@ def cpu_baseline(w, g, kept_pairs_all, dense_flops, budget_rows):
     toks = []
     for h, I in rows:
         lo, hi = I * B, min(w.L, (I + 1) * B) - 1
-        for t in np.linspace(lo, hi, 4).astype(int):
+        for t in np.unique(np.linspace(lo, hi, tokens_per_row).astype(int)):
             toks.append((h, int(t)))
     t0 = time.perf_counter()
     oracle.attention(g["q"], g["k"], g["v"], B, mask, toks=toks)
@@ -99,10 +129,10 @@ def cpu_baseline(w, g, kept_pairs_all, dense_flops, budget_rows):
     T = (t_pool + t_est * est_all / est_smp + t_sel * est_all / est_smp
          + t_att * pairs_all / max(1.0, pairs_smp))
     sample = ("oracle E1 on all keys; E2-E5 on %d block-rows (every %d-th row of every head, plus "
-              "the last) = %.2f%% of the estimation work; E6 on %d tokens (4 per sampled block-row) "
+              "the last) = %.2f%% of the estimation work; E6 on %d tokens (%d per sampled block-row) "
               "= %.4f%% of the attended (query, key) pairs; stage times scaled by those shares: pool %.2fs, "
               "estimate %.2fs, select %.2fs, attend %.2fs measured"
-              % (len(rows), step, 100 * est_smp / est_all, len(toks),
+              % (len(rows), step, 100 * est_smp / est_all, len(toks), tokens_per_row,
                  100 * pairs_smp / pairs_all, t_pool, t_est, t_sel, t_att))
     return dict(value=dense_flops / T / 1e12, unit="TFLOP/s (dense-equivalent)", cores=threads,
                 kind="oracle", sample=sample, seconds_full_workload=T)
@@ -117,7 +147,9 @@ def main():
     ap.add_argument("--S", type=int, default=None)
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
-    ap.add_argument("--cpu-rows", type=int, default=16, help="sampled block-rows per head")
+    ap.add_argument("--cpu-rows", type=int, default=32, help="sampled block-rows per head")
+    ap.add_argument("--dense", choices=["on", "off"], default="on",
+                    help="also time rr_sparse_attn with every causal block kept (tau = 1)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, copy q (known size) once: the reference dispatch for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -203,6 +235,25 @@ def main():
     torch.cuda.synchronize()
     prefill_ms = pe[0].elapsed_time(pe[1]) / args.steps
 
+    # The same attention kernel over every causal block: the dense baseline.
+    dense_ms = None
+    if args.dense == "on":
+        I = torch.arange(nb, dtype=torch.int32, device=dev)
+        counts_d = (I + 1).expand(Hq, nb).contiguous()
+        idx_d = torch.where(I[None, :] <= I[:, None], I[None, :], torch.full_like(I, -1)[None, :])
+        idx_d = idx_d.expand(Hq, nb, nb).contiguous()
+        rr.rr_sparse_attn(q, k, v, B, counts_d, idx_d, out=O, ws=ws)
+        de = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        nd = max(1, min(3, args.steps))
+        de[0].record()
+        for _ in range(nd):
+            rr.rr_sparse_attn(q, k, v, B, counts_d, idx_d, out=O, ws=ws)
+        de[1].record()
+        torch.cuda.synchronize()
+        dense_ms = de[0].elapsed_time(de[1]) / nd
+        del counts_d, idx_d
+        log("dense attention (every causal block): %.3f ms" % dense_ms)
+
     if args.copy_calibration:
         qc = torch.empty_like(q)
         torch.cuda.synchronize()
@@ -219,6 +270,7 @@ def main():
     alg_bytes_est = (L * Hkv * d * 2 + (L // S) * Hq * d * 2 + Hq * nb * (nb + 1) // 2 * 4 * 2
                      + Hq * nb * 4 + Hq * nb * (nb + 1) // 2 * 4)
     score_ms = float(est.mean() + sel.mean())
+    est_traffic = measured_traffic(w.name, EST_TRAFFIC, "traffic_bytes_per_step")
     out = {
         "metric": "sparse prefill attn ms/layer + dense-equiv TFLOP/s at 128K; scoring GB/s",
         "value": dense_flops / (ms * 1e-3) / 1e12,
@@ -237,14 +289,24 @@ def main():
         "stages_ms": {"estimate": float(est.mean()), "select": float(sel.mean()),
                       "attend": att_ms, "prefill_single_call": prefill_ms,
                       "wall_per_step": 1e3 * wall / args.steps},
+        "stages_ms_median": {"step": float(np.median(tot)), "estimate": float(np.median(est)),
+                             "select": float(np.median(sel)), "attend": float(np.median(att))},
+        "stages_ms_min": {"step": float(tot.min()), "estimate": float(est.min()),
+                          "select": float(sel.min()), "attend": float(att.min())},
+        "dense_attention_ms": dense_ms,
+        "speedup_vs_dense_attention": None if dense_ms is None else dense_ms / ms,
         "density": n_kept / causal_blocks,
         "kept_blocks": n_kept,
         "kept_diagonal_blocks": n_diag,
         "scoring": {"ms": score_ms, "algorithmic_bytes": alg_bytes_est,
-                    "GBps_algorithmic": alg_bytes_est / (score_ms * 1e-3) / 1e9},
+                    "GBps_algorithmic": alg_bytes_est / (score_ms * 1e-3) / 1e9,
+                    "measured_bytes": est_traffic,
+                    "GBps_measured": None if est_traffic is None else est_traffic / (score_ms * 1e-3) / 1e9,
+                    "hbm_frac_measured": None if est_traffic is None
+                    else est_traffic / (score_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
         "roofline": {"kernel": "rr_block_sparse_fa (with its V transpose)", "bound": "mfma",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic(w.name, ATTN_TRAFFIC, "traffic_bytes_per_launch"),
                      "flops_per_launch": flops_kept},
     }
     if args.cpu_baseline == "on":

@@ -71,9 +71,12 @@ __global__ __launch_bounds__(256) void rr_pool_k(const uint16_t *__restrict__ K,
     st16(dst + 2 * plane, make_uint4(lo[0], lo[1], lo[2], lo[3]));
 }
 
-// Offset of stride row i = I*C + a inside one head's packed (row, block) area.
-__device__ __forceinline__ long long packed_row_offset(int C, int I, int a) {
-    return (long long)C * I * (I + 1) / 2 + (long long)a * (I + 1);
+// Offset of the (stride row i = I*C + a, key block J <= I) entry inside one
+// head's packed area: block-row I owns C*(I+1) entries starting at
+// C*I*(I+1)/2, ordered by J then a, so the C strides of one key block are
+// contiguous (one 16-row MFMA tile stores 16 adjacent entries).
+__device__ __forceinline__ long long packed_offset(int C, int I, int a, int J) {
+    return (long long)C * I * (I + 1) / 2 + (long long)J * C + a;
 }
 
 // ---------------------------------------------------------------------------
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(256) void rr_score(const uint16_t *__restrict__ Q,
     auto write_stat = [&](int rt, int J, float m, float z) {
         if (lg == 0 && row_i[rt] >= 0 && J * C <= row_i[rt] && m != -INFINITY) {
             const int I = row_i[rt] / C, a = row_i[rt] - I * C;
-            stats[(size_t)row_h[rt] * P + packed_row_offset(C, I, a) + J] = make_float2(m, z);
+            stats[(size_t)row_h[rt] * P + packed_offset(C, I, a, J)] = make_float2(m, z);
             merge_max_sum(rM[rt], rZ[rt], m, z);
         }
     };
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(256) void rr_score(const uint16_t *__restrict__ Q,
                     const bool writer = (C == 8) ? ((lg & 1) == 0) : true;
                     if (writer && row_i[rt] >= 0 && mr != -INFINITY) {
                         const int I = row_i[rt] / C, a = row_i[rt] - I * C;
-                        stats[(size_t)row_h[rt] * P + packed_row_offset(C, I, a) + J] = make_float2(m, z);
+                        stats[(size_t)row_h[rt] * P + packed_offset(C, I, a, J)] = make_float2(m, z);
                         merge_max_sum(rM[rt], rZ[rt], m, z);
                     }
                 }
@@ -324,8 +327,11 @@ __global__ __launch_bounds__(256) void rr_score(const uint16_t *__restrict__ Q,
 // rr_stride_softmax_pool: one work-group per (block-row I, query head h).
 // A[h][I][J] = sum_a z(a,J) 2^(m(a,J) - M_a) / Z_a over the strides a of
 // block I, i.e. the causal softmax of each sampled row summed over the
-// block's strides.  Threads walk J, so each (row, J) pair is read once and
-// coalesced.  Entries J > I are written as zero.
+// block's strides.  Thread p of a pass reads packed entry p (J = p / C,
+// a = p % C), so the block-row's entries are read once, coalesced; the C
+// terms of one J are summed by a fixed butterfly over lanes (and, for
+// C = 128, over the two waves holding the halves), so the result does not
+// depend on timing.  Entries J > I are written as zero.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void rr_stride_softmax_pool(const float2 *__restrict__ stats,
                                                               const float2 *__restrict__ rowstat,
@@ -334,6 +340,7 @@ __global__ __launch_bounds__(256) void rr_stride_softmax_pool(const float2 *__re
     const int I = blockIdx.x, h = blockIdx.y;
     const int cI = min(C, ns - I * C);
     __shared__ float sM[128], sInvZ[128];
+    __shared__ float part[4];
     for (int a = threadIdx.x; a < cI; a += blockDim.x) {
         float2 rs = rowstat[(size_t)h * ns + I * C + a];
         sM[a] = rs.x;
@@ -342,16 +349,32 @@ __global__ __launch_bounds__(256) void rr_stride_softmax_pool(const float2 *__re
     __syncthreads();
     const float2 *base = stats + (size_t)h * P + (long long)C * I * (I + 1) / 2;
     float *out = A + ((size_t)h * nb + I) * nb;
-    for (int J = threadIdx.x; J < nb; J += blockDim.x) {
-        float acc = 0.f;
-        if (J <= I) {
-            for (int a = 0; a < cI; ++a) {
-                const float2 st = base[(size_t)a * (I + 1) + J];
-                acc += st.y * fast_exp2(st.x - sM[a]) * sInvZ[a];
-            }
+    const int span = (I + 1) * C;
+    const int lg2C = __builtin_ctz(C);
+    const int group = C < kWave ? C : kWave;  // lanes summed by the butterfly
+    for (int p0 = 0; p0 < span; p0 += 256) {
+        const int p = p0 + (int)threadIdx.x;
+        const int J = p >> lg2C, a = p & (C - 1);
+        float v = 0.f;
+        if (p < span && a < cI) {
+            const float2 st = base[p];
+            v = st.y * fast_exp2(st.x - sM[a]) * sInvZ[a];
         }
-        out[J] = acc;
+        for (int o = 1; o < group; o <<= 1) v += xor_lane(v, o);
+        if (C <= kWave) {
+            if (p < span && (a & (group - 1)) == 0) out[J] = v;
+        } else {
+            // C == 128: waves 2k and 2k+1 hold the two halves of one J.
+            if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = v;
+            __syncthreads();
+            if (threadIdx.x < 2) {
+                const int Jo = (p0 >> lg2C) + (int)threadIdx.x;
+                if (Jo <= I) out[Jo] = part[2 * threadIdx.x] + part[2 * threadIdx.x + 1];
+            }
+            __syncthreads();
+        }
     }
+    for (int J = I + 1 + (int)threadIdx.x; J < nb; J += blockDim.x) out[J] = 0.f;
 }
 
 // ---------------------------------------------------------------------------

@@ -19,7 +19,8 @@ struct Shape {
     int ns;   // L / S strides
     int c;    // B / S strides per block
     int c_last;        // strides in the last block
-    long long P;       // packed (row, key-block) entries per head
+    long long P;       // packed (row, key-block) entries per head: c * nb(nb+1)/2
+                       // (a short last block keeps the full stride c)
 };
 
 inline Shape make_shape(int L, int Hq, int Hkv, int d, int B, int S) {
@@ -30,7 +31,7 @@ inline Shape make_shape(int L, int Hq, int Hkv, int d, int B, int S) {
     s.ns = L / S;
     s.c = B / S;
     s.c_last = s.ns - (s.nb - 1) * s.c;
-    s.P = (long long)s.c * (s.nb - 1) * s.nb / 2 + (long long)s.c_last * s.nb;
+    s.P = (long long)s.c * s.nb * (s.nb + 1) / 2;
     return s;
 }
 
