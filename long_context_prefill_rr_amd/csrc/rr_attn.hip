@@ -6,9 +6,12 @@
 // within a kept block it is exact causal softmax attention with scale
 // 1/sqrt(d), and query head h reads kv-head h / (Hq/Hkv) (GQA).
 //
-// Work-group = one (query head h, query block I): BLK/32 waves, each owning 32
-// query rows.  Kept key blocks are walked in ascending order in stages of 64
-// keys:
+// Work-group = one (kv-head g, query block I, pair of query heads of g): two
+// groups of BLK/32 waves, one per head, each wave owning 32 query rows.  The
+// two heads' kept lists are merged in LDS into their union (ascending key
+// blocks, each tagged with the heads that keep it); the work-group walks the
+// union in stages of 64 keys and every K/V stage brought on chip serves both
+// heads, while a wave skips the stages its own head did not keep.
 //   * the K tile [64 keys][d] and the V^T tile [d][64 keys] of the next stage
 //     are copied global -> LDS by global_load_lds_dwordx4 (no registers) into
 //     the second of two buffers while the current stage is computed; rows
@@ -26,11 +29,11 @@
 // O^T stays in registers (one query column per lane) and is divided by the
 // softmax sum at the end.
 //
-// Grid order: kv-head major, block-row descending, the G query heads of one
-// (g, I) pair adjacent and on the same XCD (work-groups are dealt to the 8
-// XCDs round-robin), so the K/V tiles they share are served from that XCD's
-// L2 and one kv-head's K/V (64 MiB at 128K) stays in the last-level cache
-// while its rows run; long rows start first.
+// Grid order: kv-head major, block-row descending, the head pairs of one
+// (g, I) adjacent and on the same XCD (work-groups are dealt to the 8 XCDs
+// round-robin), so the K/V tiles they share are served from that XCD's L2
+// and one kv-head's K/V (64 MiB at 128K) stays in the last-level cache while
+// its rows run; long rows start first.
 #include "rr_device.h"
 #include "rr_internal.h"
 
