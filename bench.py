@@ -150,6 +150,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=32, help="sampled block-rows per head")
     ap.add_argument("--dense", choices=["on", "off"], default="on",
                     help="also time rr_sparse_attn with every causal block kept (tau = 1)")
+    ap.add_argument("--quality", choices=["on", "off"], default="on",
+                    help="after timing, score the kept blocks against Top-tau on the exact "
+                         "block mass (rr_estimate with S = 1)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, copy q (known size) once: the reference dispatch for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -254,6 +257,29 @@ def main():
         del counts_d, idx_d
         log("dense attention (every causal block): %.3f ms" % dense_ms)
 
+    # Selection quality (untimed): the step's mask against Top-tau on the exact
+    # block mass, which rr_estimate gives at S = 1.
+    quality = None
+    if args.quality == "on":
+        ws1 = torch.empty(rr.estimate_workspace_bytes(L, Hq, Hkv, d, B, 1), dtype=torch.uint8,
+                          device=dev)
+        qe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        qe[0].record()
+        exact = rr.rr_estimate(q, k, B, 1, ws=ws1)
+        qe[1].record()
+        del ws1
+        c_ref, i_ref = rr.rr_select(exact, L, B, tau)
+        _, qtot = rr.rr_mask_quality(counts, idx, c_ref, i_ref, exact, L, B)
+        torch.cuda.synchronize()
+        quality = rr.quality_summary(qtot.cpu().numpy(), Hq * nb)
+        quality["reference"] = "Top-tau (same tau) on the exact block mass (rr_estimate with S = 1)"
+        quality["exact_mass_ms"] = qe[0].elapsed_time(qe[1])
+        del exact, c_ref, i_ref
+        log("selection quality vs exact-mass Top-tau: precision %.4f recall %.4f F1 %.4f, "
+            "mass kept %.4f (min %.4f)" % (quality["precision"], quality["recall"], quality["f1"],
+                                           quality["mass_recovered_mean"],
+                                           quality["mass_recovered_min"]))
+
     if args.copy_calibration:
         qc = torch.empty_like(q)
         torch.cuda.synchronize()
@@ -296,6 +322,7 @@ def main():
         "dense_attention_ms": dense_ms,
         "speedup_vs_dense_attention": None if dense_ms is None else dense_ms / ms,
         "density": n_kept / causal_blocks,
+        "selection_quality": quality,
         "kept_blocks": n_kept,
         "kept_diagonal_blocks": n_diag,
         "scoring": {"ms": score_ms, "algorithmic_bytes": alg_bytes_est,

@@ -124,6 +124,33 @@ int rr_prefill(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, i
                int d, int B, int S, float tau, void *O, int o_dtype, int32_t *counts,
                int32_t *block_idx, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * rr_mask_quality -- how well a kept-block mask matches a reference mask and
+ * how much block mass it keeps (precision and F1 of the selected blocks,
+ * RRAttention summary page, Key points).  The intended reference is the
+ * Top-tau selection on the exact attention mass of every block: rr_estimate
+ * with S = 1 samples every token and pools nothing, so its block scores are
+ * the exact causal softmax mass of each B x B block; rr_select on them with
+ * the same tau gives the reference mask.
+ * Per (head h, block-row I), over distinct listed blocks J with 0 <= J <= I
+ * (entries past the count, out of range or repeated are ignored):
+ *   kept  = blocks of the tested mask, ref = blocks of the reference mask,
+ *   both  = blocks in both,
+ *   share = sum of mass[h][I][J] over the tested mask's blocks
+ *           / sum of mass[h][I][J] over all J <= I (0 if that sum is 0).
+ *   counts, block_idx          in, the tested mask (layout of rr_select).
+ *   ref_counts, ref_block_idx  in, the reference mask (same layout).
+ *   mass                       in, fp32 [Hq][nb][nb] block mass (J <= I read).
+ *   rows                       out, fp32 [Hq][nb][4]: kept, ref, both, share.
+ *   totals                     out, fp64 [5]: sums of kept, ref, both and
+ *                              share over all rows, then the minimum share.
+ *                              Summed in a fixed order (reproducible).
+ * Precision = both / kept, recall = both / ref, F1 = 2 both / (kept + ref).
+ */
+int rr_mask_quality(const int32_t *counts, const int32_t *block_idx, const int32_t *ref_counts,
+                    const int32_t *ref_block_idx, const float *mass, int Hq, int L, int B,
+                    float *rows, double *totals, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -151,4 +151,18 @@ int rr_prefill(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, i
     return run_attn(Q, K, V, s, counts, block_idx, O, o_dtype, rest, st);
 }
 
+int rr_mask_quality(const int32_t *counts, const int32_t *block_idx, const int32_t *ref_counts,
+                    const int32_t *ref_block_idx, const float *mass, int Hq, int L, int B,
+                    float *rows, double *totals, void *stream) {
+    if (!counts || !block_idx || !ref_counts || !ref_block_idx || !mass || !rows || !totals)
+        return RR_E_NULL;
+    if (L <= 0 || Hq <= 0 || B <= 0) return RR_E_SHAPE;
+    const int nb = (L + B - 1) / B;
+    if (nb > kMaxBlocks) return RR_E_UNSUPPORTED;
+    if (launch_mask_quality(counts, block_idx, ref_counts, ref_block_idx, mass, Hq, nb, rows,
+                            totals, as_stream(stream)) != hipSuccess)
+        return RR_E_HIP;
+    return RR_OK;
+}
+
 }  // extern "C"

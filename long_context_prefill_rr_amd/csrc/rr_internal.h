@@ -39,7 +39,7 @@ inline Shape make_shape(int L, int Hq, int Hkv, int d, int B, int S) {
 // pairs and per-row (max, sum) pairs.
 struct EstimateWs {
     uint16_t *kplanes;  // [3][Hkv][ns][d] bf16 (hi, mid, lo split of the fp32 mean)
-    float2 *stats;      // [Hq][P] packed, row i = I*c + a owns entries J = 0..I
+    float2 *stats;      // [Hq][P] packed: block-row I owns c*(I+1) entries, J-major
     float2 *rowstat;    // [Hq][ns]
 };
 
@@ -72,5 +72,9 @@ hipError_t launch_transpose_v(const uint16_t *V, const Shape &s, uint16_t *Vt, h
 hipError_t launch_block_sparse_fa(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt,
                                   const Shape &s, const int32_t *counts, const int32_t *block_idx,
                                   void *O, bool out_f32, hipStream_t st);
+hipError_t launch_mask_quality(const int32_t *counts, const int32_t *block_idx,
+                               const int32_t *ref_counts, const int32_t *ref_idx,
+                               const float *mass, int Hq, int nb, float *rows, double *totals,
+                               hipStream_t st);
 
 }  // namespace rr

@@ -1,4 +1,4 @@
-"""ctypes binding of librr.so: the same four calls as the C ABI (include/rr.h).
+"""ctypes binding of librr.so: the same calls as the C ABI (include/rr.h).
 
 Every function only checks tensor placement, dtype and contiguity, allocates
 outputs and workspace with torch when the caller does not pass them, and
@@ -60,7 +60,8 @@ def _load():
         lib.rr_select.argtypes = [P, i, i, i, f, P, P, P]
         lib.rr_sparse_attn.argtypes = [P, P, P, i, i, i, i, i, P, P, P, i, P, z, P]
         lib.rr_prefill.argtypes = [P, P, P, i, i, i, i, i, i, f, P, i, P, P, P, z, P]
-        for name in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill"):
+        lib.rr_mask_quality.argtypes = [P, P, P, P, P, i, i, i, P, P, P]
+        for name in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill", "rr_mask_quality"):
             getattr(lib, name).restype = i
         _lib = lib
     return _lib
@@ -187,3 +188,37 @@ def rr_prefill(q, k, v, B, S, tau, out=None, out_dtype=torch.bfloat16, counts=No
                         ws.numel() * ws.element_size(), _stream_ptr(stream))
     _check(rc, "rr_prefill")
     return out, counts, block_idx
+
+
+def rr_mask_quality(counts, block_idx, ref_counts, ref_block_idx, mass, L, B, rows=None,
+                    totals=None, stream=None):
+    """Per-row (kept, ref, both, kept mass share) [Hq][nb][4] fp32 and their
+    totals [5] fp64 (sums of the four columns, then the minimum share)."""
+    Hq, nb = counts.shape
+    dev = counts.device
+    if rows is None:
+        rows = torch.empty((Hq, nb, 4), dtype=torch.float32, device=dev)
+    if totals is None:
+        totals = torch.empty(5, dtype=torch.float64, device=dev)
+    rc = _load().rr_mask_quality(_dev(counts, "counts", torch.int32),
+                                 _dev(block_idx, "block_idx", torch.int32),
+                                 _dev(ref_counts, "ref_counts", torch.int32),
+                                 _dev(ref_block_idx, "ref_block_idx", torch.int32),
+                                 _dev(mass, "mass", torch.float32), Hq, L, B,
+                                 _dev(rows, "rows", torch.float32),
+                                 _dev(totals, "totals", torch.float64), _stream_ptr(stream))
+    _check(rc, "rr_mask_quality")
+    return rows, totals
+
+
+def quality_summary(totals, n_rows):
+    """Precision, recall, F1 and mean / minimum kept mass share from the
+    totals of rr_mask_quality (host arithmetic on five numbers)."""
+    kept, ref, both, share, share_min = [float(x) for x in totals]
+    return {"precision": both / kept if kept else 0.0,
+            "recall": both / ref if ref else 0.0,
+            "f1": 2.0 * both / (kept + ref) if kept + ref else 0.0,
+            "mass_recovered_mean": share / n_rows if n_rows else 0.0,
+            "mass_recovered_min": share_min,
+            "kept_blocks": int(round(kept)), "reference_blocks": int(round(ref)),
+            "common_blocks": int(round(both))}

@@ -6,5 +6,5 @@ for the definitions each function follows.
 """
 from .oracle import (  # noqa: F401
     build, lib_path, pool_keys, stride_scores, block_scores, select, attention,
-    set_threads, get_threads, mask_from_list, list_from_mask,
+    set_threads, get_threads, mask_from_list, list_from_mask, mask_quality, quality_metrics,
 )

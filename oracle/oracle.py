@@ -184,3 +184,44 @@ def list_from_mask(mask):
             js = np.nonzero(mask[h, I])[0]
             idx[h, I, :len(js)] = js
     return counts, idx
+
+
+def mask_quality(mask, ref_mask, mass):
+    """Selection quality of a block mask against a reference mask (the
+    precision and F1 of selected blocks reported on the RRAttention summary
+    page, Key points), written out from the definitions in fp64.
+
+    mask, ref_mask: [Hq][nb][nb] 0/1, only causal entries J <= I count.
+    mass: [Hq][nb][nb] block mass (e.g. block_scores with S = 1, the exact
+    causal attention mass of each block).
+
+    Returns (rows [Hq][nb][4] = kept, ref, both, share of the row's causal
+    mass in the kept blocks; totals [5] = column sums and the minimum share).
+    """
+    mask = np.asarray(mask).astype(bool)
+    ref_mask = np.asarray(ref_mask).astype(bool)
+    mass = np.asarray(mass, dtype=np.float64)
+    Hq, nb, _ = mask.shape
+    rows = np.zeros((Hq, nb, 4), dtype=np.float64)
+    for h in range(Hq):
+        for I in range(nb):
+            t = mask[h, I, :I + 1]
+            r = ref_mask[h, I, :I + 1]
+            a = mass[h, I, :I + 1]
+            w = a.sum()
+            rows[h, I, 0] = t.sum()
+            rows[h, I, 1] = r.sum()
+            rows[h, I, 2] = (t & r).sum()
+            rows[h, I, 3] = a[t].sum() / w if w > 0 else 0.0
+    flat = rows.reshape(-1, 4)
+    totals = np.array([flat[:, 0].sum(), flat[:, 1].sum(), flat[:, 2].sum(), flat[:, 3].sum(),
+                       flat[:, 3].min()])
+    return rows, totals
+
+
+def quality_metrics(totals, n_rows):
+    """Precision = both/kept, recall = both/ref, F1 = 2 both/(kept + ref),
+    and the mean kept mass share per row."""
+    kept, ref, both, share, share_min = [float(x) for x in totals]
+    return {"precision": both / kept, "recall": both / ref, "f1": 2.0 * both / (kept + ref),
+            "mass_recovered_mean": share / n_rows, "mass_recovered_min": share_min}

@@ -29,9 +29,9 @@ def lib():
     return rr.load_library()
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill"):
+    for n in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill", "rr_mask_quality"):
         assert n in names
 
 
@@ -112,3 +112,18 @@ def test_python_binding_rejects_cpu_tensors():
     q = torch.zeros((128, 2, 64), dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         rr.rr_estimate(q, q, 64, 8)
+
+
+def test_mask_quality_validation(lib):
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, 1024, 128, FAKE, FAKE, None]
+    a = list(args); a[4] = None
+    assert lib.rr_mask_quality(*a) == RR_E_NULL
+    a = list(args); a[9] = None
+    assert lib.rr_mask_quality(*a) == RR_E_NULL
+    a = list(args); a[5] = 0
+    assert lib.rr_mask_quality(*a) == RR_E_SHAPE
+    a = list(args); a[7] = -1
+    assert lib.rr_mask_quality(*a) == RR_E_SHAPE
+    a = list(args); a[6] = 128 * 4097
+    assert lib.rr_mask_quality(*a) == RR_E_UNSUPPORTED
+
