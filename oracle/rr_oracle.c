@@ -26,7 +26,11 @@
  *            sampled queries and keys, aggregation per stride.
  *  [XA-tb]   XAttention review page, section "threshold block selection",
  *            formal definition of find_blocks: the smallest set of blocks
- *            whose summed attention probability reaches tau.
+ *            whose summed attention probability reaches tau; its steps 1-2
+ *            (antidiagonal sums per S x S sub-block, softmax over the sums).
+ *  [XA-is]   XAttention review page, "importance prediction": elements are
+ *            picked along the antidiagonal of each sub-block with stride S
+ *            and their sum stands for the block's importance.
  *
  * Readings where the pages are silent (each is also listed in the design
  * notes of the repository):
@@ -241,6 +245,115 @@ int rro_block_scores(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hk
         free(p);
     }
     free(KbarT);
+    return err;
+}
+
+/*
+ * X1 -- XAttention's antidiagonal stride scoring [XA-is: XAttention review
+ * page, "importance prediction", and "threshold block selection" step 1].
+ * Inside every S x S sub-block of the attention map the elements on the
+ * antidiagonal (lower-left to upper-right) are summed as the sub-block's
+ * importance.  Sub-block (i, j) spans query tokens iS..iS+S-1 and key tokens
+ * jS..jS+S-1, so its antidiagonal pairs query iS+t with key jS+S-1-t.
+ * Reading: the elements summed are the scaled logits (1/sqrt(d)) q.k (the
+ * next step applies the softmax to the sums).  For j <= i:
+ *   x[j] = (1/sqrt(d)) * sum_{t<S} sum_k Q[iS+t][h][k] * K[jS+S-1-t][g(h)][k]
+ * summed over t, then k, in ascending order.  Kd is K widened to double,
+ * [L][Hkv][d]; qrow receives the S query rows of stride i.
+ */
+static void xattn_stride_scores(const uint16_t *Q, const double *Kd, int Hq, int Hkv, int d,
+                                int S, int h, int i, double *qrow, double *x)
+{
+    int g = h / (Hq / Hkv);
+    double sc = 1.0 / sqrt((double)d);
+    for (int t = 0; t < S; ++t)
+        for (int k = 0; k < d; ++k)
+            qrow[(size_t)t * d + k] = bf16_value(Q[((size_t)(i * S + t) * Hq + h) * d + k]);
+    for (int j = 0; j <= i; ++j) {
+        double acc = 0.0;
+        for (int t = 0; t < S; ++t) {
+            const double *kk = Kd + ((size_t)(j * S + S - 1 - t) * Hkv + g) * d;
+            const double *q = qrow + (size_t)t * d;
+            for (int k = 0; k < d; ++k) acc += q[k] * kk[k];
+        }
+        x[j] = sc * acc;
+    }
+}
+
+static double *widen_keys(const uint16_t *K, int L, int Hkv, int d)
+{
+    size_t n = (size_t)L * Hkv * d;
+    double *Kd = (double *)malloc(sizeof(double) * n);
+    if (!Kd) return NULL;
+    for (size_t e = 0; e < n; ++e) Kd[e] = bf16_value(K[e]);
+    return Kd;
+}
+
+/* X1 alone, for tests: antidiagonal scores x[0..i] of stride row i, head h. */
+int rro_xattn_stride_scores(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv,
+                            int d, int S, int h, int i, double *x)
+{
+    if (!Q || !K || !x || !shape_ok(L, Hq, Hkv, d, S, S)) return RRO_E_ARG;
+    int ns = L / S;
+    if (h < 0 || h >= Hq || i < 0 || i >= ns) return RRO_E_ARG;
+    double *Kd = widen_keys(K, L, Hkv, d);
+    double *qrow = (double *)malloc(sizeof(double) * (size_t)S * d);
+    if (!Kd || !qrow) {
+        free(Kd);
+        free(qrow);
+        return RRO_E_NOMEM;
+    }
+    xattn_stride_scores(Q, Kd, Hq, Hkv, d, S, h, i, qrow, x);
+    free(Kd);
+    free(qrow);
+    return RRO_OK;
+}
+
+/*
+ * X1 + E3 + E4 -- XAttention block scores [XA-tb steps 1-2: antidiagonal
+ * sums, then a softmax over them; pooled to B x B blocks as for E4].  The
+ * softmax runs over the causal strides j <= i of stride row i (E3) and its
+ * probabilities are summed over the c x c sub-blocks of each block (E4), so
+ * each block-row again sums to c_I.  Same row list and output layout as
+ * rro_block_scores.
+ */
+int rro_xattn_block_scores(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv,
+                           int d, int B, int S, const int32_t *rows, int nrows, double *A)
+{
+    if (!Q || !K || !rows || !A || nrows < 0 || !shape_ok(L, Hq, Hkv, d, B, S)) return RRO_E_ARG;
+    int ns = L / S, c = B / S, nb = (L + B - 1) / B;
+    for (int r = 0; r < nrows; ++r)
+        if (rows[2 * r] < 0 || rows[2 * r] >= Hq || rows[2 * r + 1] < 0 || rows[2 * r + 1] >= nb)
+            return RRO_E_ARG;
+    double *Kd = widen_keys(K, L, Hkv, d);
+    if (!Kd) return RRO_E_NOMEM;
+    int err = RRO_OK;
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)ns);
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)S * d);
+        if (!p || !qrow) {
+#pragma omp atomic write
+            err = RRO_E_NOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < nrows; ++r) {
+            if (!p || !qrow) continue;
+            int h = rows[2 * r], I = rows[2 * r + 1];
+            double *Arow = A + (size_t)r * nb;
+            for (int J = 0; J < nb; ++J) Arow[J] = 0.0;
+            for (int a = 0; a < c; ++a) {
+                int i = I * c + a;
+                if (i >= ns) break;
+                xattn_stride_scores(Q, Kd, Hq, Hkv, d, S, h, i, qrow, p);
+                causal_softmax(p, i);
+                for (int j = 0; j <= i; ++j) Arow[j / c] += p[j];
+            }
+        }
+        free(p);
+        free(qrow);
+    }
+    free(Kd);
     return err;
 }
 

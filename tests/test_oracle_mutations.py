@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "rr_oracle.c")
 PINS = ["tests/test_oracle_estimate.py", "tests/test_oracle_select.py",
-        "tests/test_oracle_attention.py"]
+        "tests/test_oracle_attention.py", "tests/test_oracle_xattn.py"]
 
 MUTANTS = [
     ("E1 sum instead of mean", "Kbar[((size_t)g * ns + j) * d + k] = sum / (double)S;",
@@ -41,6 +41,12 @@ MUTANTS = [
     ("E6 strict causality", "for (int nn = 0; nn <= t; ++nn) {\n                if (!mrow[nn / B]) continue;\n                const uint16_t *kr",
      "for (int nn = 0; nn < t; ++nn) {\n                if (!mrow[nn / B]) continue;\n                const uint16_t *kr"),
     ("E6 missing scale", "l[nn] = sigma * dot;", "l[nn] = dot;"),
+    ("X1 main diagonal", "const double *kk = Kd + ((size_t)(j * S + S - 1 - t) * Hkv + g) * d;",
+     "const double *kk = Kd + ((size_t)(j * S + t) * Hkv + g) * d;"),
+    ("X1 missing scale", "x[j] = sc * acc;", "x[j] = acc;"),
+    ("X1 wrong kv-head", "int g = h / (Hq / Hkv);", "int g = h % Hkv;"),
+    ("X1 one query per stride", "bf16_value(Q[((size_t)(i * S + t) * Hq + h) * d + k]);",
+     "bf16_value(Q[((size_t)(i * S) * Hq + h) * d + k]);"),
     ("E6 mask ignored", "            for (int nn = 0; nn <= t; ++nn) {\n                if (!mrow[nn / B]) continue;\n                double p",
      "            for (int nn = 0; nn <= t; ++nn) {\n                if (!mrow[t / B]) continue;\n                double p"),
 ]
