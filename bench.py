@@ -150,6 +150,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=32, help="sampled block-rows per head")
     ap.add_argument("--dense", choices=["on", "off"], default="on",
                     help="also time rr_sparse_attn with every causal block kept (tau = 1)")
+    ap.add_argument("--xattn", choices=["on", "off"], default="on",
+                    help="also time XAttention's antidiagonal estimate + Top-tau on the same "
+                         "inputs (the pattern search the pages compare against)")
     ap.add_argument("--quality", choices=["on", "off"], default="on",
                     help="after timing, score the kept blocks against Top-tau on the exact "
                          "block mass (rr_estimate with S = 1)")
@@ -257,7 +260,43 @@ def main():
         del counts_d, idx_d
         log("dense attention (every causal block): %.3f ms" % dense_ms)
 
-    # Selection quality (untimed): the step's mask against Top-tau on the exact
+    # XAttention's antidiagonal estimate on the same inputs and Top-tau, under
+    # both readings of its softmax input (antidiagonal sum, antidiagonal mean).
+    xattn = None
+    xmasks = {}
+    if args.xattn == "on" and B // S in (8, 16, 32):
+        Ax = torch.empty_like(A)
+        rr_search = float(est.mean() + sel.mean())
+        xattn = {"rr_pattern_search_ms": rr_search,
+                 "estimate_flop": 2.0 * S * d * Hq * (L // S) * (L // S + 1) / 2.0}
+        for reading, avg in (("sum", False), ("mean", True)):
+            cx, ix = torch.empty_like(counts), torch.empty_like(idx)
+            for _ in range(args.warmup):
+                rr.rr_xattn_estimate(q, k, B, S, block_scores=Ax, ws=ws, average=avg)
+                rr.rr_select(Ax, L, B, tau, counts=cx, block_idx=ix)
+            xev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+            for e in xev:
+                e[0].record()
+                rr.rr_xattn_estimate(q, k, B, S, block_scores=Ax, ws=ws, average=avg)
+                e[1].record()
+                rr.rr_select(Ax, L, B, tau, counts=cx, block_idx=ix)
+                e[2].record()
+            torch.cuda.synchronize()
+            xest = np.array([e[0].elapsed_time(e[1]) for e in xev])
+            xsel = np.array([e[1].elapsed_time(e[2]) for e in xev])
+            _, nkx, _ = kept_block_flops(cx, ix, L, B, d)
+            x_search = float(xest.mean() + xsel.mean())
+            xattn[reading] = {"estimate_ms": float(xest.mean()), "select_ms": float(xsel.mean()),
+                              "pattern_search_ms": x_search,
+                              "rr_search_time_reduction": 1.0 - rr_search / x_search,
+                              "density": nkx / (Hq * nb * (nb + 1) // 2)}
+            xmasks[reading] = (cx, ix)
+            log("xattn (%s) estimate %.3f ms + select %.3f ms (round-robin %.3f ms): density %.4f"
+                % (reading, xattn[reading]["estimate_ms"], xattn[reading]["select_ms"], rr_search,
+                   xattn[reading]["density"]))
+        del Ax
+
+    # Selection quality (untimed): each mask against Top-tau on the exact
     # block mass, which rr_estimate gives at S = 1.
     quality = None
     if args.quality == "on":
@@ -274,11 +313,20 @@ def main():
         quality = rr.quality_summary(qtot.cpu().numpy(), Hq * nb)
         quality["reference"] = "Top-tau (same tau) on the exact block mass (rr_estimate with S = 1)"
         quality["exact_mass_ms"] = qe[0].elapsed_time(qe[1])
-        del exact, c_ref, i_ref
         log("selection quality vs exact-mass Top-tau: precision %.4f recall %.4f F1 %.4f, "
             "mass kept %.4f (min %.4f)" % (quality["precision"], quality["recall"], quality["f1"],
                                            quality["mass_recovered_mean"],
                                            quality["mass_recovered_min"]))
+        for reading, (cx, ix) in xmasks.items():
+            _, qtx = rr.rr_mask_quality(cx, ix, c_ref, i_ref, exact, L, B)
+            torch.cuda.synchronize()
+            xattn[reading]["selection_quality"] = rr.quality_summary(qtx.cpu().numpy(), Hq * nb)
+            xq = xattn[reading]["selection_quality"]
+            log("xattn (%s) selection quality: precision %.4f recall %.4f F1 %.4f, mass kept %.4f "
+                "(min %.4f)" % (reading, xq["precision"], xq["recall"], xq["f1"],
+                                xq["mass_recovered_mean"], xq["mass_recovered_min"]))
+        del exact, c_ref, i_ref
+    xmasks.clear()
 
     if args.copy_calibration:
         qc = torch.empty_like(q)
@@ -323,6 +371,7 @@ def main():
         "speedup_vs_dense_attention": None if dense_ms is None else dense_ms / ms,
         "density": n_kept / causal_blocks,
         "selection_quality": quality,
+        "xattn_comparison": xattn,
         "kept_blocks": n_kept,
         "kept_diagonal_blocks": n_diag,
         "scoring": {"ms": score_ms, "algorithmic_bytes": alg_bytes_est,

@@ -125,6 +125,27 @@ int rr_prefill(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, i
                int32_t *block_idx, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * rr_xattn_estimate -- XAttention's antidiagonal block scores (XAttention
+ * review page, "importance prediction" and "threshold block selection"
+ * steps 1-2), the estimator the RRAttention pages compare against, on the
+ * same softmax pooling so that rr_select and rr_sparse_attn consume it
+ * unchanged.  Inside each S x S sub-block (i, j) of the attention map the
+ * antidiagonal logits are summed: x[h][i][j] = (1/sqrt(d)) * sum_{t<S}
+ * Q[iS+t][h] . K[jS+S-1-t][g]; each stride row i is normalised by a softmax
+ * over j <= i and the probabilities are summed over B x B blocks.
+ *   average       0: the antidiagonal sum as the page states it; nonzero:
+ *                 the sum divided by S (mean logit, so the softmax keeps the
+ *                 temperature of single tokens), an alternative reading.
+ *   block_scores  out, fp32 [Hq][nb][nb], as for rr_estimate.
+ *   ws, ws_bytes  device workspace, >= rr_estimate_workspace_bytes(...).
+ * Supported: B/S in {8, 16, 32} (S = 4, 8, 16 at B = 128), else
+ * RR_E_UNSUPPORTED; other shape rules as for rr_estimate.
+ */
+int rr_xattn_estimate(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv, int d, int B,
+                      int S, int average, float *block_scores, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/*
  * rr_mask_quality -- how well a kept-block mask matches a reference mask and
  * how much block mass it keeps (precision and F1 of the selected blocks,
  * RRAttention summary page, Key points).  The intended reference is the

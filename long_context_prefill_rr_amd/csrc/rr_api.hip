@@ -165,4 +165,21 @@ int rr_mask_quality(const int32_t *counts, const int32_t *block_idx, const int32
     return RR_OK;
 }
 
+int rr_xattn_estimate(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv, int d, int B,
+                      int S, int average, float *block_scores, void *ws, size_t ws_bytes,
+                      void *stream) {
+    if (!Q || !K || !block_scores || !ws) return RR_E_NULL;
+    int rc = check_shape(L, Hq, Hkv, d, B, S, true);
+    if (rc != RR_OK) return rc;
+    const int c = B / S;
+    if (c != 8 && c != 16 && c != 32) return RR_E_UNSUPPORTED;
+    const Shape s = make_shape(L, Hq, Hkv, d, B, S);
+    if (ws_bytes < estimate_ws_bytes(s)) return RR_E_WORKSPACE;
+    const EstimateWs w = carve_estimate(s, ws);
+    hipStream_t st = as_stream(stream);
+    if (launch_xscore(Q, K, s, average != 0, w, st) != hipSuccess) return RR_E_HIP;
+    if (launch_softmax_pool(s, w, block_scores, st) != hipSuccess) return RR_E_HIP;
+    return RR_OK;
+}
+
 }  // extern "C"

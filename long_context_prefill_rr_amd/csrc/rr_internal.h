@@ -72,6 +72,8 @@ hipError_t launch_transpose_v(const uint16_t *V, const Shape &s, uint16_t *Vt, h
 hipError_t launch_block_sparse_fa(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt,
                                   const Shape &s, const int32_t *counts, const int32_t *block_idx,
                                   void *O, bool out_f32, hipStream_t st);
+hipError_t launch_xscore(const uint16_t *Q, const uint16_t *K, const Shape &s, bool average,
+                         const EstimateWs &w, hipStream_t st);
 hipError_t launch_mask_quality(const int32_t *counts, const int32_t *block_idx,
                                const int32_t *ref_counts, const int32_t *ref_idx,
                                const float *mass, int Hq, int nb, float *rows, double *totals,

@@ -61,7 +61,9 @@ def _load():
         lib.rr_sparse_attn.argtypes = [P, P, P, i, i, i, i, i, P, P, P, i, P, z, P]
         lib.rr_prefill.argtypes = [P, P, P, i, i, i, i, i, i, f, P, i, P, P, P, z, P]
         lib.rr_mask_quality.argtypes = [P, P, P, P, P, i, i, i, P, P, P]
-        for name in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill", "rr_mask_quality"):
+        lib.rr_xattn_estimate.argtypes = [P, P, i, i, i, i, i, i, i, P, P, z, P]
+        for name in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill", "rr_mask_quality",
+                     "rr_xattn_estimate"):
             getattr(lib, name).restype = i
         _lib = lib
     return _lib
@@ -120,6 +122,24 @@ def rr_estimate(q, k, B, S, block_scores=None, ws=None, stream=None):
                          d, B, S, _dev(block_scores, "block_scores", torch.float32),
                          _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream_ptr(stream))
     _check(rc, "rr_estimate")
+    return block_scores
+
+
+def rr_xattn_estimate(q, k, B, S, block_scores=None, ws=None, stream=None, average=False):
+    """Block scores [Hq][nb][nb] (fp32) of XAttention's antidiagonal estimate
+    (average=True: antidiagonal mean instead of sum)."""
+    L, Hq, d = q.shape
+    Hkv = k.shape[1]
+    nb = -(-L // B)
+    if block_scores is None:
+        block_scores = torch.empty((Hq, nb, nb), dtype=torch.float32, device=q.device)
+    lib = _load()
+    ws = _workspace(lib.rr_estimate_workspace_bytes(L, Hq, Hkv, d, B, S), q.device, ws)
+    rc = lib.rr_xattn_estimate(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), L, Hq,
+                               Hkv, d, B, S, int(bool(average)),
+                               _dev(block_scores, "block_scores", torch.float32),
+                               _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream_ptr(stream))
+    _check(rc, "rr_xattn_estimate")
     return block_scores
 
 

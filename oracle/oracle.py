@@ -46,8 +46,8 @@ def _load():
         lib.rro_pool_keys.argtypes = [P, i, i, i, i, P]
         lib.rro_stride_scores.argtypes = [P, P, i, i, i, i, i, i, i, P]
         lib.rro_block_scores.argtypes = [P, P, i, i, i, i, i, i, P, i, P]
-        lib.rro_xattn_stride_scores.argtypes = [P, P, i, i, i, i, i, i, i, P]
-        lib.rro_xattn_block_scores.argtypes = [P, P, i, i, i, i, i, i, P, i, P]
+        lib.rro_xattn_stride_scores.argtypes = [P, P, i, i, i, i, i, i, i, i, P]
+        lib.rro_xattn_block_scores.argtypes = [P, P, i, i, i, i, i, i, i, P, i, P]
         lib.rro_select.argtypes = [P, P, i, i, ctypes.c_double, P, P, P]
         lib.rro_attention.argtypes = [P, P, P, i, i, i, i, i, P, P, i, P]
         lib.rro_set_threads.argtypes = [i]
@@ -122,18 +122,19 @@ def block_scores(q, k, B, S, rows=None):
     return out.reshape(Hq, nb, nb) if full else out
 
 
-def xattn_stride_scores(q, k, S, h, i):
-    """X1: XAttention antidiagonal scores x[0..i] of stride row i, head h."""
+def xattn_stride_scores(q, k, S, h, i, average=False):
+    """X1: XAttention antidiagonal scores x[0..i] of stride row i, head h
+    (average=True divides each antidiagonal sum by S)."""
     q, k = _u16(q), _u16(k)
     L, Hq, d = q.shape
     Hkv = k.shape[1]
     out = np.empty(i + 1, dtype=np.float64)
-    _check(_load().rro_xattn_stride_scores(_ptr(q), _ptr(k), L, Hq, Hkv, d, S, h, i,
-                                           _ptr(out)), "xattn_stride_scores")
+    _check(_load().rro_xattn_stride_scores(_ptr(q), _ptr(k), L, Hq, Hkv, d, S, int(average), h,
+                                           i, _ptr(out)), "xattn_stride_scores")
     return out
 
 
-def xattn_block_scores(q, k, B, S, rows=None):
+def xattn_block_scores(q, k, B, S, rows=None, average=False):
     """X1 + E3 + E4: XAttention block scores, same layout as block_scores."""
     q, k = _u16(q), _u16(k)
     L, Hq, d = q.shape
@@ -144,8 +145,9 @@ def xattn_block_scores(q, k, B, S, rows=None):
         rows = [(h, I) for h in range(Hq) for I in range(nb)]
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
     out = np.empty((rows.shape[0], nb), dtype=np.float64)
-    _check(_load().rro_xattn_block_scores(_ptr(q), _ptr(k), L, Hq, Hkv, d, B, S, _ptr(rows),
-                                          rows.shape[0], _ptr(out)), "xattn_block_scores")
+    _check(_load().rro_xattn_block_scores(_ptr(q), _ptr(k), L, Hq, Hkv, d, B, S, int(average),
+                                          _ptr(rows), rows.shape[0], _ptr(out)),
+           "xattn_block_scores")
     return out.reshape(Hq, nb, nb) if full else out
 
 

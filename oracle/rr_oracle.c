@@ -258,14 +258,18 @@ int rro_block_scores(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hk
  * Reading: the elements summed are the scaled logits (1/sqrt(d)) q.k (the
  * next step applies the softmax to the sums).  For j <= i:
  *   x[j] = (1/sqrt(d)) * sum_{t<S} sum_k Q[iS+t][h][k] * K[jS+S-1-t][g(h)][k]
- * summed over t, then k, in ascending order.  Kd is K widened to double,
- * [L][Hkv][d]; qrow receives the S query rows of stride i.
+ * summed over t, then k, in ascending order.  With average != 0 the sum is
+ * divided by S (the mean antidiagonal logit, which keeps the softmax at the
+ * temperature of single tokens), an alternative reading of the same step.
+ * Kd is K widened to double, [L][Hkv][d]; qrow receives the S query rows of
+ * stride i.
  */
 static void xattn_stride_scores(const uint16_t *Q, const double *Kd, int Hq, int Hkv, int d,
-                                int S, int h, int i, double *qrow, double *x)
+                                int S, int average, int h, int i, double *qrow, double *x)
 {
     int g = h / (Hq / Hkv);
     double sc = 1.0 / sqrt((double)d);
+    if (average) sc /= (double)S;
     for (int t = 0; t < S; ++t)
         for (int k = 0; k < d; ++k)
             qrow[(size_t)t * d + k] = bf16_value(Q[((size_t)(i * S + t) * Hq + h) * d + k]);
@@ -291,7 +295,7 @@ static double *widen_keys(const uint16_t *K, int L, int Hkv, int d)
 
 /* X1 alone, for tests: antidiagonal scores x[0..i] of stride row i, head h. */
 int rro_xattn_stride_scores(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv,
-                            int d, int S, int h, int i, double *x)
+                            int d, int S, int average, int h, int i, double *x)
 {
     if (!Q || !K || !x || !shape_ok(L, Hq, Hkv, d, S, S)) return RRO_E_ARG;
     int ns = L / S;
@@ -303,7 +307,7 @@ int rro_xattn_stride_scores(const uint16_t *Q, const uint16_t *K, int L, int Hq,
         free(qrow);
         return RRO_E_NOMEM;
     }
-    xattn_stride_scores(Q, Kd, Hq, Hkv, d, S, h, i, qrow, x);
+    xattn_stride_scores(Q, Kd, Hq, Hkv, d, S, average, h, i, qrow, x);
     free(Kd);
     free(qrow);
     return RRO_OK;
@@ -318,7 +322,8 @@ int rro_xattn_stride_scores(const uint16_t *Q, const uint16_t *K, int L, int Hq,
  * rro_block_scores.
  */
 int rro_xattn_block_scores(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv,
-                           int d, int B, int S, const int32_t *rows, int nrows, double *A)
+                           int d, int B, int S, int average, const int32_t *rows, int nrows,
+                           double *A)
 {
     if (!Q || !K || !rows || !A || nrows < 0 || !shape_ok(L, Hq, Hkv, d, B, S)) return RRO_E_ARG;
     int ns = L / S, c = B / S, nb = (L + B - 1) / B;
@@ -345,7 +350,7 @@ int rro_xattn_block_scores(const uint16_t *Q, const uint16_t *K, int L, int Hq, 
             for (int a = 0; a < c; ++a) {
                 int i = I * c + a;
                 if (i >= ns) break;
-                xattn_stride_scores(Q, Kd, Hq, Hkv, d, S, h, i, qrow, p);
+                xattn_stride_scores(Q, Kd, Hq, Hkv, d, S, average, h, i, qrow, p);
                 causal_softmax(p, i);
                 for (int j = 0; j <= i; ++j) Arow[j / c] += p[j];
             }

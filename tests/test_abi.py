@@ -31,7 +31,8 @@ def lib():
 
 def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill", "rr_mask_quality"):
+    for n in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill", "rr_mask_quality",
+              "rr_xattn_estimate"):
         assert n in names
 
 
@@ -126,4 +127,15 @@ def test_mask_quality_validation(lib):
     assert lib.rr_mask_quality(*a) == RR_E_SHAPE
     a = list(args); a[6] = 128 * 4097
     assert lib.rr_mask_quality(*a) == RR_E_UNSUPPORTED
+
+
+def test_xattn_estimate_validation(lib):
+    def x(L=1024, S=8, B=128, Q=FAKE, ws_bytes=1 << 40, d=128):
+        return lib.rr_xattn_estimate(Q, FAKE, L, 8, 2, d, B, S, 0, FAKE, FAKE, ws_bytes, None)
+    assert x(Q=None) == RR_E_NULL
+    assert x(S=1) == RR_E_UNSUPPORTED       # B/S = 128: no instantiation
+    assert x(S=2) == RR_E_UNSUPPORTED       # B/S = 64
+    assert x(L=1004) == RR_E_SHAPE          # L % S
+    assert x(d=96) == RR_E_UNSUPPORTED
+    assert x(ws_bytes=16) == RR_E_WORKSPACE
 

@@ -44,6 +44,7 @@ MUTANTS = [
     ("X1 main diagonal", "const double *kk = Kd + ((size_t)(j * S + S - 1 - t) * Hkv + g) * d;",
      "const double *kk = Kd + ((size_t)(j * S + t) * Hkv + g) * d;"),
     ("X1 missing scale", "x[j] = sc * acc;", "x[j] = acc;"),
+    ("X1 average ignored", "    if (average) sc /= (double)S;\n", "\n"),
     ("X1 wrong kv-head", "int g = h / (Hq / Hkv);", "int g = h % Hkv;"),
     ("X1 one query per stride", "bf16_value(Q[((size_t)(i * S + t) * Hq + h) * d + k]);",
      "bf16_value(Q[((size_t)(i * S) * Hq + h) * d + k]);"),

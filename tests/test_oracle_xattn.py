@@ -37,6 +37,8 @@ def test_antidiagonal_matches_brute_force(S, L):
             main_diag = np.array([sum(logits[i * S + u, j * S + u] for u in range(S))
                                   for j in range(i + 1)])
             assert not np.allclose(got, main_diag)
+            mean = oracle.xattn_stride_scores(g["q"], g["k"], S, h, i, average=True)
+            np.testing.assert_allclose(mean, want / S, rtol=1e-12, atol=1e-12)
 
 
 def _exact_block_mass(q, k, B, Hq, Hkv):
@@ -53,11 +55,11 @@ def _exact_block_mass(q, k, B, Hq, Hkv):
     return Pp.reshape(Hq, nb, B, nb, B).sum(axis=(2, 4))
 
 
-@pytest.mark.parametrize("L,B", [(256, 64), (288, 64)])
-def test_stride_one_is_exact_block_mass(L, B):
+@pytest.mark.parametrize("L,B,average", [(256, 64, False), (288, 64, False), (256, 64, True)])
+def test_stride_one_is_exact_block_mass(L, B, average):
     # With S = 1 each sub-block is one logit: the estimate is exact attention.
     w, g = small_workload(L=L, Hq=4, Hkv=2, d=32, B=B, S=1)
-    A = oracle.xattn_block_scores(g["q"], g["k"], B, 1)
+    A = oracle.xattn_block_scores(g["q"], g["k"], B, 1, average=average)
     want = _exact_block_mass(to_f64(g["q"]), to_f64(g["k"]), B, w.Hq, w.Hkv)
     np.testing.assert_allclose(A, want, rtol=1e-10, atol=1e-12)
 
@@ -78,12 +80,15 @@ def test_stride_constant_inputs_scale_round_robin_scores():
             x = oracle.xattn_stride_scores(Q, K, S, h, i)
             s = oracle.stride_scores(Q, K, S, h, i)
             np.testing.assert_allclose(x, S * s, rtol=1e-12, atol=1e-12)
+            xm = oracle.xattn_stride_scores(Q, K, S, h, i, average=True)
+            np.testing.assert_allclose(xm, s, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("S,B,L", [(8, 64, 512), (4, 64, 320), (16, 128, 1024)])
-def test_rows_sum_to_strides_and_row_list(S, B, L):
+@pytest.mark.parametrize("S,B,L,average", [(8, 64, 512, False), (4, 64, 320, False),
+                                           (16, 128, 1024, False), (8, 64, 512, True)])
+def test_rows_sum_to_strides_and_row_list(S, B, L, average):
     w, g = small_workload(L=L, Hq=4, Hkv=2, d=32, B=B, S=S, seed=9)
-    A = oracle.xattn_block_scores(g["q"], g["k"], B, S)
+    A = oracle.xattn_block_scores(g["q"], g["k"], B, S, average=average)
     c = B // S
     ns = L // S
     for I in range(w.nb):
@@ -92,7 +97,7 @@ def test_rows_sum_to_strides_and_row_list(S, B, L):
         assert np.all(A[:, I, I + 1:] == 0)
     assert A.min() >= 0
     rows = [(3, w.nb - 1), (0, 0), (2, 1)]
-    Ar = oracle.xattn_block_scores(g["q"], g["k"], B, S, rows=rows)
+    Ar = oracle.xattn_block_scores(g["q"], g["k"], B, S, rows=rows, average=average)
     for r, (h, I) in enumerate(rows):
         np.testing.assert_array_equal(Ar[r], A[h, I])
 
