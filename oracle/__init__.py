@@ -6,6 +6,6 @@ for the definitions each function follows.
 """
 from .oracle import (  # noqa: F401
     build, lib_path, pool_keys, stride_scores, block_scores, select, attention,
-    xattn_stride_scores, xattn_block_scores,
+    xattn_stride_scores, xattn_block_scores, rescue_scores, union_masks,
     set_threads, get_threads, mask_from_list, list_from_mask, mask_quality, quality_metrics,
 )

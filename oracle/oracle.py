@@ -49,11 +49,12 @@ def _load():
         lib.rro_xattn_stride_scores.argtypes = [P, P, i, i, i, i, i, i, i, i, P]
         lib.rro_xattn_block_scores.argtypes = [P, P, i, i, i, i, i, i, i, P, i, P]
         lib.rro_select.argtypes = [P, P, i, i, ctypes.c_double, P, P, P]
+        lib.rro_rescue_scores.argtypes = [P, P, i, i, i, i, i, P]
         lib.rro_attention.argtypes = [P, P, P, i, i, i, i, i, P, P, i, P]
         lib.rro_set_threads.argtypes = [i]
         lib.rro_get_threads.restype = i
         for f in ("rro_pool_keys", "rro_stride_scores", "rro_block_scores", "rro_select",
-                  "rro_xattn_stride_scores", "rro_xattn_block_scores",
+                  "rro_xattn_stride_scores", "rro_xattn_block_scores", "rro_rescue_scores",
                   "rro_attention"):
             getattr(lib, f).restype = i
         _lib = lib
@@ -149,6 +150,26 @@ def xattn_block_scores(q, k, B, S, rows=None, average=False):
                                           _ptr(rows), rows.shape[0], _ptr(out)),
            "xattn_block_scores")
     return out.reshape(Hq, nb, nb) if full else out
+
+
+def rescue_scores(q, k, B):
+    """R1: RBS rescue-branch scores [Hq][nb][nb] (softmax over J <= I of the
+    radius upper-bound logits)."""
+    q, k = _u16(q), _u16(k)
+    L, Hq, d = q.shape
+    Hkv = k.shape[1]
+    nb = -(-L // B)
+    out = np.empty((Hq, nb, nb), dtype=np.float64)
+    _check(_load().rro_rescue_scores(_ptr(q), _ptr(k), L, Hq, Hkv, d, B, _ptr(out)),
+           "rescue_scores")
+    return out
+
+
+def union_masks(a, b):
+    """Combined mask of two selection branches: a block is kept when either
+    branch keeps it (RBS-Attention page: the two branches' masks are
+    combined)."""
+    return (np.asarray(a).astype(bool) | np.asarray(b).astype(bool)).astype(np.uint8)
 
 
 def select(A, tau, I_of_row=None):

@@ -28,6 +28,9 @@
  *            formal definition of find_blocks: the smallest set of blocks
  *            whose summed attention probability reaches tau; its steps 1-2
  *            (antidiagonal sums per S x S sub-block, softmax over the sums).
+ *  [RBS-abs] RBS-Attention page, abstract and method summary: centroid base
+ *            branch, rescue branch from the maximum key-block radius,
+ *            independent thresholds, masks combined.
  *  [XA-is]   XAttention review page, "importance prediction": elements are
  *            picked along the antidiagonal of each sub-block with stride S
  *            and their sum stands for the block's importance.
@@ -360,6 +363,97 @@ int rro_xattn_block_scores(const uint16_t *Q, const uint16_t *K, int L, int Hq, 
     }
     free(Kd);
     return err;
+}
+
+/*
+ * R1 -- RBS-Attention's rescue branch [RBS-abs: RBS-Attention page, abstract
+ * and method summary: a block centroid can hide one highly relevant key
+ * among many irrelevant ones ("mean dilution"); a rescue branch uses the
+ * maximum key-block radius to flag blocks at risk of underestimation, is
+ * thresholded independently of the base branch, and its mask is combined
+ * with the base mask].  Reading (the page gives no formula): with the
+ * centroid kc_J of the keys of block J (kv-head g(h)), its radius
+ * r_J = max_{n in J} ||K[n] - kc_J||_2, and the mean query qc_I of block I
+ * (head h), the rescue logit is the largest logit qc_I can reach against a
+ * key of block J (Cauchy-Schwarz):
+ *   u[h][I][J] = (1/sqrt(d)) * (qc_I . kc_J + ||qc_I||_2 * r_J),  J <= I,
+ * and the rescue scores are its softmax over J <= I (each row sums to 1),
+ * ready for the same Top-tau rule (E5) with the rescue branch's own tau.
+ * A short last block averages its real tokens only.  Out: A [Hq][nb][nb],
+ * zeros for J > I.
+ */
+int rro_rescue_scores(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv, int d,
+                      int B, double *A)
+{
+    if (!Q || !K || !A || !shape_ok(L, Hq, Hkv, d, B, 1)) return RRO_E_ARG;
+    int nb = (L + B - 1) / B, G = Hq / Hkv;
+    double *kc = (double *)calloc((size_t)Hkv * nb * d, sizeof(double));
+    double *rad = (double *)calloc((size_t)Hkv * nb, sizeof(double));
+    double *qc = (double *)calloc((size_t)Hq * nb * d, sizeof(double));
+    if (!kc || !rad || !qc) {
+        free(kc);
+        free(rad);
+        free(qc);
+        return RRO_E_NOMEM;
+    }
+    for (int g = 0; g < Hkv; ++g)
+        for (int J = 0; J < nb; ++J) {
+            int n0 = J * B, n1 = (J + 1) * B < L ? (J + 1) * B : L;
+            double *c = kc + ((size_t)g * nb + J) * d;
+            for (int n = n0; n < n1; ++n)
+                for (int k = 0; k < d; ++k) c[k] += bf16_value(K[((size_t)n * Hkv + g) * d + k]);
+            for (int k = 0; k < d; ++k) c[k] /= (double)(n1 - n0);
+            double r = 0.0;
+            for (int n = n0; n < n1; ++n) {
+                double s2 = 0.0;
+                for (int k = 0; k < d; ++k) {
+                    double e = bf16_value(K[((size_t)n * Hkv + g) * d + k]) - c[k];
+                    s2 += e * e;
+                }
+                if (sqrt(s2) > r) r = sqrt(s2);
+            }
+            rad[(size_t)g * nb + J] = r;
+        }
+    for (int h = 0; h < Hq; ++h)
+        for (int I = 0; I < nb; ++I) {
+            int t0 = I * B, t1 = (I + 1) * B < L ? (I + 1) * B : L;
+            double *c = qc + ((size_t)h * nb + I) * d;
+            for (int t = t0; t < t1; ++t)
+                for (int k = 0; k < d; ++k) c[k] += bf16_value(Q[((size_t)t * Hq + h) * d + k]);
+            for (int k = 0; k < d; ++k) c[k] /= (double)(t1 - t0);
+        }
+    double sigma = 1.0 / sqrt((double)d);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < Hq * nb; ++r) {
+        int h = r / nb, I = r % nb, g = h / G;
+        const double *q = qc + (size_t)r * d;
+        double qn = 0.0;
+        for (int k = 0; k < d; ++k) qn += q[k] * q[k];
+        qn = sqrt(qn);
+        double *Arow = A + (size_t)r * nb;
+        double m = -INFINITY;
+        for (int J = 0; J < nb; ++J) {
+            if (J > I) {
+                Arow[J] = 0.0;
+                continue;
+            }
+            const double *c = kc + ((size_t)g * nb + J) * d;
+            double dot = 0.0;
+            for (int k = 0; k < d; ++k) dot += q[k] * c[k];
+            Arow[J] = sigma * (dot + qn * rad[(size_t)g * nb + J]);
+            if (Arow[J] > m) m = Arow[J];
+        }
+        double z = 0.0;
+        for (int J = 0; J <= I; ++J) {
+            Arow[J] = exp(Arow[J] - m);
+            z += Arow[J];
+        }
+        for (int J = 0; J <= I; ++J) Arow[J] /= z;
+    }
+    free(kc);
+    free(rad);
+    free(qc);
+    return RRO_OK;
 }
 
 /* Ordering of E5: larger block score first, then smaller block index. */

@@ -14,7 +14,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "rr_oracle.c")
 PINS = ["tests/test_oracle_estimate.py", "tests/test_oracle_select.py",
-        "tests/test_oracle_attention.py", "tests/test_oracle_xattn.py"]
+        "tests/test_oracle_attention.py", "tests/test_oracle_xattn.py",
+        "tests/test_oracle_rescue.py"]
 
 MUTANTS = [
     ("E1 sum instead of mean", "Kbar[((size_t)g * ns + j) * d + k] = sum / (double)S;",
@@ -48,6 +49,12 @@ MUTANTS = [
     ("X1 wrong kv-head", "int g = h / (Hq / Hkv);", "int g = h % Hkv;"),
     ("X1 one query per stride", "bf16_value(Q[((size_t)(i * S + t) * Hq + h) * d + k]);",
      "bf16_value(Q[((size_t)(i * S) * Hq + h) * d + k]);"),
+    ("R1 radius ignored", "Arow[J] = sigma * (dot + qn * rad[(size_t)g * nb + J]);",
+     "Arow[J] = sigma * dot;"),
+    ("R1 short block divided by B", "for (int k = 0; k < d; ++k) c[k] /= (double)(n1 - n0);",
+     "for (int k = 0; k < d; ++k) c[k] /= (double)B;"),
+    ("R1 radius as mean distance", "if (sqrt(s2) > r) r = sqrt(s2);", "r += sqrt(s2) / (double)(n1 - n0);"),
+    ("R1 wrong kv-head", "int h = r / nb, I = r % nb, g = h / G;", "int h = r / nb, I = r % nb, g = h % Hkv;"),
     ("E6 mask ignored", "            for (int nn = 0; nn <= t; ++nn) {\n                if (!mrow[nn / B]) continue;\n                double p",
      "            for (int nn = 0; nn <= t; ++nn) {\n                if (!mrow[t / B]) continue;\n                double p"),
 ]
