@@ -153,6 +153,9 @@ def main():
     ap.add_argument("--xattn", choices=["on", "off"], default="on",
                     help="also time XAttention's antidiagonal estimate + Top-tau on the same "
                          "inputs (the pattern search the pages compare against)")
+    ap.add_argument("--rescue-tau", type=float, default=0.5,
+                    help="tau of the RBS-style rescue branch OR'ed into the round-robin mask "
+                         "(0 disables)")
     ap.add_argument("--quality", choices=["on", "off"], default="on",
                     help="after timing, score the kept blocks against Top-tau on the exact "
                          "block mass (rr_estimate with S = 1)")
@@ -296,6 +299,49 @@ def main():
                    xattn[reading]["density"]))
         del Ax
 
+    # RBS-style rescue branch: its own scores and Top-tau, OR'ed into the
+    # round-robin mask; then attention under the combined mask.
+    rescue = None
+    rmask = None
+    if args.rescue_tau > 0:
+        Ar = torch.empty_like(A)
+        wsr = torch.empty(rr.rescue_workspace_bytes(L, Hq, Hkv, d, B), dtype=torch.uint8, device=dev)
+        cr, ir = torch.empty_like(counts), torch.empty_like(idx)
+        cu, iu = torch.empty_like(counts), torch.empty_like(idx)
+
+        def rescue_step():
+            rr.rr_rescue_estimate(q, k, B, block_scores=Ar, ws=wsr)
+            rr.rr_select(Ar, L, B, args.rescue_tau, counts=cr, block_idx=ir)
+            rr.rr_merge_masks(counts, idx, cr, ir, L, B, counts=cu, block_idx=iu)
+
+        for _ in range(args.warmup):
+            rescue_step()
+        re_ = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        re_[0].record()
+        for _ in range(args.steps):
+            rescue_step()
+        re_[1].record()
+        rr.rr_sparse_attn(q, k, v, B, cu, iu, out=O, ws=ws)
+        ae = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ae[0].record()
+        for _ in range(max(1, min(3, args.steps))):
+            rr.rr_sparse_attn(q, k, v, B, cu, iu, out=O, ws=ws)
+        ae[1].record()
+        torch.cuda.synchronize()
+        _, nku, _ = kept_block_flops(cu, iu, L, B, d)
+        _, nkr, _ = kept_block_flops(cr, ir, L, B, d)
+        rescue = {"tau": args.rescue_tau,
+                  "rescue_branch_ms": re_[0].elapsed_time(re_[1]) / args.steps,
+                  "rescue_density": nkr / (Hq * nb * (nb + 1) // 2),
+                  "union_density": nku / (Hq * nb * (nb + 1) // 2),
+                  "union_attention_ms": ae[0].elapsed_time(ae[1]) / max(1, min(3, args.steps))}
+        rmask = (cu, iu)
+        del Ar, wsr, cr, ir
+        log("rescue branch (tau %.2f) %.3f ms: rescue density %.4f, union density %.4f, attention "
+            "under the union %.3f ms" % (args.rescue_tau, rescue["rescue_branch_ms"],
+                                         rescue["rescue_density"], rescue["union_density"],
+                                         rescue["union_attention_ms"]))
+
     # Selection quality (untimed): each mask against Top-tau on the exact
     # block mass, which rr_estimate gives at S = 1.
     quality = None
@@ -317,6 +363,14 @@ def main():
             "mass kept %.4f (min %.4f)" % (quality["precision"], quality["recall"], quality["f1"],
                                            quality["mass_recovered_mean"],
                                            quality["mass_recovered_min"]))
+        if rmask is not None:
+            _, qtr = rr.rr_mask_quality(rmask[0], rmask[1], c_ref, i_ref, exact, L, B)
+            torch.cuda.synchronize()
+            rescue["union_selection_quality"] = rr.quality_summary(qtr.cpu().numpy(), Hq * nb)
+            uq = rescue["union_selection_quality"]
+            log("union selection quality: precision %.4f recall %.4f F1 %.4f, mass kept %.4f "
+                "(min %.4f)" % (uq["precision"], uq["recall"], uq["f1"],
+                                uq["mass_recovered_mean"], uq["mass_recovered_min"]))
         for reading, (cx, ix) in xmasks.items():
             _, qtx = rr.rr_mask_quality(cx, ix, c_ref, i_ref, exact, L, B)
             torch.cuda.synchronize()
@@ -327,6 +381,7 @@ def main():
                                 xq["mass_recovered_mean"], xq["mass_recovered_min"]))
         del exact, c_ref, i_ref
     xmasks.clear()
+    rmask = None
 
     if args.copy_calibration:
         qc = torch.empty_like(q)
@@ -372,6 +427,7 @@ def main():
         "density": n_kept / causal_blocks,
         "selection_quality": quality,
         "xattn_comparison": xattn,
+        "rescue_branch": rescue,
         "kept_blocks": n_kept,
         "kept_diagonal_blocks": n_diag,
         "scoring": {"ms": score_ms, "algorithmic_bytes": alg_bytes_est,

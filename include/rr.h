@@ -146,6 +146,38 @@ int rr_xattn_estimate(const uint16_t *Q, const uint16_t *K, int L, int Hq, int H
                       void *stream);
 
 /*
+ * rr_rescue_estimate -- block scores of an RBS-style rescue branch (RBS-
+ * Attention page, abstract and method summary: a block centroid can hide one
+ * highly relevant key, so a second branch built on the maximum key-block
+ * radius flags blocks at risk; the branches are thresholded independently and
+ * their masks combined).  The page gives no formula; the reading taken here:
+ *   u[h][I][J] = (1/sqrt(d)) * (qc . kc_J + ||qc|| * r_J),   J <= I,
+ * with qc the mean query of block I (head h), kc_J the mean key of block J
+ * (kv-head g), r_J = max over the keys of block J of ||K[n] - kc_J||: the
+ * largest logit qc can reach against a key of block J.  block_scores[h][I]
+ * is the softmax of u over J <= I (rows sum to 1, zeros for J > I), so
+ * rr_select keeps blocks with the branch's own tau and rr_merge_masks ORs
+ * the result into another mask.  A short last block uses its own tokens.
+ *   ws, ws_bytes  device workspace, >= rr_rescue_workspace_bytes(...).
+ * Shapes: d in {64, 128}, B in {64, 128}, nb <= 4096 (no stride here).
+ */
+size_t rr_rescue_workspace_bytes(int L, int Hq, int Hkv, int d, int B);
+int rr_rescue_estimate(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv, int d, int B,
+                       float *block_scores, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * rr_merge_masks -- union of two kept-block masks given as lists (the
+ * combined mask of two selection branches, RBS-Attention page).  Per (h, I)
+ * the output lists every block J (0 <= J <= I) that either input lists, in
+ * ascending order with -1 after counts[h][I] (the layout of rr_select).
+ * Input entries past their count, out of range or repeated are ignored.
+ * Outputs must not alias the inputs.
+ */
+int rr_merge_masks(const int32_t *counts_a, const int32_t *block_idx_a, const int32_t *counts_b,
+                   const int32_t *block_idx_b, int Hq, int L, int B, int32_t *counts,
+                   int32_t *block_idx, void *stream);
+
+/*
  * rr_mask_quality -- how well a kept-block mask matches a reference mask and
  * how much block mass it keeps (precision and F1 of the selected blocks,
  * RRAttention summary page, Key points).  The intended reference is the

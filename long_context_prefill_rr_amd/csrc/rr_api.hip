@@ -182,4 +182,35 @@ int rr_xattn_estimate(const uint16_t *Q, const uint16_t *K, int L, int Hq, int H
     return RR_OK;
 }
 
+size_t rr_rescue_workspace_bytes(int L, int Hq, int Hkv, int d, int B) {
+    if (check_shape(L, Hq, Hkv, d, B, 1, false) != RR_OK) return 0;
+    return rescue_ws_bytes(make_shape(L, Hq, Hkv, d, B, 1));
+}
+
+int rr_rescue_estimate(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv, int d, int B,
+                       float *block_scores, void *ws, size_t ws_bytes, void *stream) {
+    if (!Q || !K || !block_scores || !ws) return RR_E_NULL;
+    int rc = check_shape(L, Hq, Hkv, d, B, 1, false);
+    if (rc != RR_OK) return rc;
+    const Shape s = make_shape(L, Hq, Hkv, d, B, 1);
+    if (ws_bytes < rescue_ws_bytes(s)) return RR_E_WORKSPACE;
+    if (launch_rescue(Q, K, s, (float *)ws, block_scores, as_stream(stream)) != hipSuccess)
+        return RR_E_HIP;
+    return RR_OK;
+}
+
+int rr_merge_masks(const int32_t *counts_a, const int32_t *block_idx_a, const int32_t *counts_b,
+                   const int32_t *block_idx_b, int Hq, int L, int B, int32_t *counts,
+                   int32_t *block_idx, void *stream) {
+    if (!counts_a || !block_idx_a || !counts_b || !block_idx_b || !counts || !block_idx)
+        return RR_E_NULL;
+    if (L <= 0 || Hq <= 0 || B <= 0) return RR_E_SHAPE;
+    const int nb = (L + B - 1) / B;
+    if (nb > kMaxBlocks) return RR_E_UNSUPPORTED;
+    if (launch_merge_lists(counts_a, block_idx_a, counts_b, block_idx_b, Hq, nb, counts,
+                           block_idx, as_stream(stream)) != hipSuccess)
+        return RR_E_HIP;
+    return RR_OK;
+}
+
 }  // extern "C"

@@ -74,6 +74,15 @@ hipError_t launch_block_sparse_fa(const uint16_t *Q, const uint16_t *K, const ui
                                   void *O, bool out_f32, hipStream_t st);
 hipError_t launch_xscore(const uint16_t *Q, const uint16_t *K, const Shape &s, bool average,
                          const EstimateWs &w, hipStream_t st);
+// Rescue workspace: block centroids of Q and K (fp32) and key-block radii.
+inline size_t rescue_ws_bytes(const Shape &s) {
+    return align_up(((size_t)(s.Hq + s.Hkv) * s.nb * s.d + (size_t)s.Hkv * s.nb) * 4);
+}
+hipError_t launch_rescue(const uint16_t *Q, const uint16_t *K, const Shape &s, float *ws,
+                         float *A, hipStream_t st);
+hipError_t launch_merge_lists(const int32_t *ca, const int32_t *ia, const int32_t *cb,
+                              const int32_t *ib, int Hq, int nb, int32_t *co, int32_t *io,
+                              hipStream_t st);
 hipError_t launch_mask_quality(const int32_t *counts, const int32_t *block_idx,
                                const int32_t *ref_counts, const int32_t *ref_idx,
                                const float *mass, int Hq, int nb, float *rows, double *totals,

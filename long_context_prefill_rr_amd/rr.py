@@ -62,8 +62,12 @@ def _load():
         lib.rr_prefill.argtypes = [P, P, P, i, i, i, i, i, i, f, P, i, P, P, P, z, P]
         lib.rr_mask_quality.argtypes = [P, P, P, P, P, i, i, i, P, P, P]
         lib.rr_xattn_estimate.argtypes = [P, P, i, i, i, i, i, i, i, P, P, z, P]
+        lib.rr_rescue_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.rr_rescue_workspace_bytes.restype = z
+        lib.rr_rescue_estimate.argtypes = [P, P, i, i, i, i, i, P, P, z, P]
+        lib.rr_merge_masks.argtypes = [P, P, P, P, i, i, i, P, P, P]
         for name in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill", "rr_mask_quality",
-                     "rr_xattn_estimate"):
+                     "rr_xattn_estimate", "rr_rescue_estimate", "rr_merge_masks"):
             getattr(lib, name).restype = i
         _lib = lib
     return _lib
@@ -95,6 +99,10 @@ def estimate_workspace_bytes(L, Hq, Hkv, d, B, S):
 
 def sparse_attn_workspace_bytes(L, Hq, Hkv, d, B):
     return _load().rr_sparse_attn_workspace_bytes(L, Hq, Hkv, d, B)
+
+
+def rescue_workspace_bytes(L, Hq, Hkv, d, B):
+    return _load().rr_rescue_workspace_bytes(L, Hq, Hkv, d, B)
 
 
 def prefill_workspace_bytes(L, Hq, Hkv, d, B, S):
@@ -242,3 +250,39 @@ def quality_summary(totals, n_rows):
             "mass_recovered_min": share_min,
             "kept_blocks": int(round(kept)), "reference_blocks": int(round(ref)),
             "common_blocks": int(round(both))}
+
+
+def rr_rescue_estimate(q, k, B, block_scores=None, ws=None, stream=None):
+    """Rescue-branch block scores [Hq][nb][nb] (fp32, rows sum to 1)."""
+    L, Hq, d = q.shape
+    Hkv = k.shape[1]
+    nb = -(-L // B)
+    if block_scores is None:
+        block_scores = torch.empty((Hq, nb, nb), dtype=torch.float32, device=q.device)
+    lib = _load()
+    ws = _workspace(lib.rr_rescue_workspace_bytes(L, Hq, Hkv, d, B), q.device, ws)
+    rc = lib.rr_rescue_estimate(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), L, Hq,
+                                Hkv, d, B, _dev(block_scores, "block_scores", torch.float32),
+                                _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream_ptr(stream))
+    _check(rc, "rr_rescue_estimate")
+    return block_scores
+
+
+def rr_merge_masks(counts_a, block_idx_a, counts_b, block_idx_b, L, B, counts=None,
+                   block_idx=None, stream=None):
+    """Union of two block lists: (counts [Hq][nb], block_idx [Hq][nb][nb])."""
+    Hq, nb = counts_a.shape
+    dev = counts_a.device
+    if counts is None:
+        counts = torch.empty((Hq, nb), dtype=torch.int32, device=dev)
+    if block_idx is None:
+        block_idx = torch.empty((Hq, nb, nb), dtype=torch.int32, device=dev)
+    rc = _load().rr_merge_masks(_dev(counts_a, "counts_a", torch.int32),
+                                _dev(block_idx_a, "block_idx_a", torch.int32),
+                                _dev(counts_b, "counts_b", torch.int32),
+                                _dev(block_idx_b, "block_idx_b", torch.int32), Hq, L, B,
+                                _dev(counts, "counts", torch.int32),
+                                _dev(block_idx, "block_idx", torch.int32), _stream_ptr(stream))
+    _check(rc, "rr_merge_masks")
+    return counts, block_idx
+

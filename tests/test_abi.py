@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill", "rr_mask_quality",
-              "rr_xattn_estimate"):
+              "rr_xattn_estimate", "rr_rescue_estimate", "rr_merge_masks"):
         assert n in names
 
 
@@ -138,4 +138,24 @@ def test_xattn_estimate_validation(lib):
     assert x(L=1004) == RR_E_SHAPE          # L % S
     assert x(d=96) == RR_E_UNSUPPORTED
     assert x(ws_bytes=16) == RR_E_WORKSPACE
+
+
+def test_rescue_and_merge_validation(lib):
+    lib.rr_rescue_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.rr_rescue_workspace_bytes(1024, 8, 2, 128, 128) == (8 + 2) * 8 * 128 * 4 + 2 * 8 * 4 or \
+        lib.rr_rescue_workspace_bytes(1024, 8, 2, 128, 128) >= (8 + 2) * 8 * 128 * 4 + 2 * 8 * 4
+    assert lib.rr_rescue_workspace_bytes(1024, 6, 4, 128, 128) == 0          # Hq % Hkv
+    r = lambda **kw: lib.rr_rescue_estimate(kw.get("Q", FAKE), FAKE, kw.get("L", 1024), 8, 2,
+                                            kw.get("d", 128), kw.get("B", 128), FAKE, FAKE,
+                                            kw.get("ws", 1 << 40), None)
+    assert r(Q=None) == RR_E_NULL
+    assert r(d=96) == RR_E_UNSUPPORTED
+    assert r(B=32) == RR_E_UNSUPPORTED
+    assert r(ws=16) == RR_E_WORKSPACE
+    assert r(L=0) == RR_E_SHAPE
+    m = lambda **kw: lib.rr_merge_masks(FAKE, FAKE, kw.get("cb", FAKE), FAKE, 8, kw.get("L", 1024),
+                                        128, FAKE, FAKE, None)
+    assert m(cb=None) == RR_E_NULL
+    assert m(L=0) == RR_E_SHAPE
+    assert m(L=128 * 4097) == RR_E_UNSUPPORTED
 
