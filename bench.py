@@ -166,7 +166,7 @@ def main():
 
     if args.gpus != 1:
         print("bench.py measures one GPU: the path shards by whole kv-head groups with no "
-              "exchange, and this build runs on a single MI355X; --gpus %d is not supported"
+              "exchange, and this benchmark measures one MI355X; --gpus %d is not supported"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 
