@@ -399,6 +399,14 @@ def main():
     alg_bytes_est = (L * Hkv * d * 2 + (L // S) * Hq * d * 2 + Hq * nb * (nb + 1) // 2 * 4 * 2
                      + Hq * nb * 4 + Hq * nb * (nb + 1) // 2 * 4)
     score_ms = float(est.mean() + sel.mean())
+    # Bytes a materialising design would move for the same result: K, the
+    # sampled Q rows, fp32 pooled keys and fp32 stride scores each written and
+    # read once, A written and read, and the lists.
+    c_ = B // S
+    ns_ = L // S
+    design_a_bytes = (L * Hkv * d * 2 + ns_ * Hq * d * 2 + 2 * ns_ * Hkv * d * 4
+                      + 2 * Hq * c_ * c_ * (nb * (nb + 1) // 2) * 4 + 2 * Hq * nb * nb * 4
+                      + Hq * nb * nb * 4)
     est_traffic = measured_traffic(w.name, EST_TRAFFIC, "traffic_bytes_per_step")
     out = {
         "metric": "sparse prefill attn ms/layer + dense-equiv TFLOP/s at 128K; scoring GB/s",
@@ -435,7 +443,10 @@ def main():
                     "measured_bytes": est_traffic,
                     "GBps_measured": None if est_traffic is None else est_traffic / (score_ms * 1e-3) / 1e9,
                     "hbm_frac_measured": None if est_traffic is None
-                    else est_traffic / (score_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+                    else est_traffic / (score_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                    "design_a_bytes": design_a_bytes,
+                    "design_a_equivalent_hbm_frac": design_a_bytes / (score_ms * 1e-3) / 1e9
+                    / HBM_PEAK_GBPS},
         "roofline": {"kernel": "rr_block_sparse_fa (with its V transpose)", "bound": "mfma",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic(w.name, ATTN_TRAFFIC, "traffic_bytes_per_launch"),
