@@ -122,10 +122,11 @@ def test_merge_of_empty_lists_is_empty():
     assert int(cu.abs().sum()) == 0 and bool((iu == -1).all())
 
 
-def test_rescue_at_full_size_sampled():
-    """128K workload: rescue scores on sampled rows against the oracle."""
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_rescue_at_full_size(cfg):
+    """128K and 64K-video workloads: every rescue score against the oracle."""
     rr = _rr()
-    w = get_config(3)
+    w = get_config(cfg)
     g = generate(w)
     q, k = _dev(g["q"]), _dev(g["k"])
     Ar = rr.rr_rescue_estimate(q, k, w.B)

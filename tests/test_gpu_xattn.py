@@ -82,7 +82,7 @@ def _rows_sample(w, every):
 
 
 @pytest.mark.parametrize("cfg,every,average", [(1, 1, False), (1, 1, True), (3, 64, False),
-                                               (3, 64, True)])
+                                               (3, 64, True), (4, 32, False), (4, 32, True)])
 def test_xattn_full_size(cfg, every, average):
     rr = _rr()
     w = get_config(cfg)
