@@ -12,10 +12,11 @@
 // blocks, each tagged with the heads that keep it); the work-group walks the
 // union in stages of 64 keys and every K/V stage brought on chip serves both
 // heads, while a wave skips the stages its own head did not keep.
-//   * the K tile [64 keys][d] and the V^T tile [d][64 keys] of the next stage
-//     are copied global -> LDS by global_load_lds_dwordx4 (no registers) into
-//     the second of two buffers while the current stage is computed; rows
-//     are XOR-swizzled in 16-byte slots against LDS bank conflicts;
+//   * the K tiles [64 keys][d] and V^T tiles [d][64 keys] of the next two
+//     stages are copied global -> LDS by buffer_load_dwordx4 ... lds (no
+//     registers) into one pair of buffers while the two stages held by the
+//     other pair are computed, with one barrier per pair of stages; rows are
+//     XOR-swizzled in 16-byte slots against LDS bank conflicts;
 //   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16.  The K rows fed to the
 //     matrix unit are permuted so that accumulator register e of lane
 //     (column q, half hk) holds key 16*hk + e of each 32-key sub-tile:
@@ -38,6 +39,9 @@
 #include "rr_internal.h"
 
 namespace rr {
+
+// K fragments are read this many d-steps ahead of the products that use them.
+constexpr int KLA = 2;
 
 // V [L][Hkv][d] -> Vt [Hkv][d][Lp], tokens >= L zero-filled.  64x64 tiles.
 __global__ __launch_bounds__(256) void rr_transpose_v(const uint16_t *__restrict__ V, int L, int Lp,
@@ -115,8 +119,12 @@ __global__ __launch_bounds__(BLK * 4, 2) void rr_block_sparse_fa(
     using C = FaCfg<D, BLK>;
     __shared__ __attribute__((aligned(1024))) char Kb0[C::KBYTES];
     __shared__ __attribute__((aligned(1024))) char Kb1[C::KBYTES];
+    __shared__ __attribute__((aligned(1024))) char Kb2[C::KBYTES];
+    __shared__ __attribute__((aligned(1024))) char Kb3[C::KBYTES];
     __shared__ __attribute__((aligned(1024))) char Vb0[C::VBYTES];
     __shared__ __attribute__((aligned(1024))) char Vb1[C::VBYTES];
+    __shared__ __attribute__((aligned(1024))) char Vb2[C::VBYTES];
+    __shared__ __attribute__((aligned(1024))) char Vb3[C::VBYTES];
     __shared__ uint32_t ulist[C::MAXNB];          // union of the two kept lists
     __shared__ uint32_t bits[2][C::MAXNB / 32];   // per-head membership bitmaps
     __shared__ int scan_part[C::NW];
@@ -225,6 +233,9 @@ __global__ __launch_bounds__(BLK * 4, 2) void rr_block_sparse_fa(
         if (st >= nst) return -1;
         return __builtin_amdgcn_readfirstlane((int)ulist[st / C::SPB]);
     };
+    // Copy target of stage st: a stage past the end re-copies the last one
+    // (into a buffer no one reads), so every step issues the same copies.
+    auto copy_stage = [&](int st) -> int { return min(st, nst - 1); };
 
     // Per-lane byte offsets of this wave's copies inside one stage (the same
     // for every stage): K chunk (row r, slot c^swz) and V^T chunk.  Each copy
@@ -245,31 +256,34 @@ __global__ __launch_bounds__(BLK * 4, 2) void rr_block_sparse_fa(
     const char *kbase = reinterpret_cast<const char *>(K + (size_t)g * D);
     const char *vbase = reinterpret_cast<const char *>(Vt + (size_t)g * D * Lp);
 
-    // Start the copies of stage st (key block J) into (kb, vb); returns false
-    // if none.
-    auto issue = [&](int st, int ent, char *kb, char *vb) -> bool {
-        if (ent < 0) return false;
+    // Start the copies of stage st (key block J) into (kb, vb).
+    auto issue = [&](int st, char *kb, char *vb) {
+        st = copy_stage(st);
+        const int ent = __builtin_amdgcn_readfirstlane((int)ulist[st / C::SPB]);
         const int J = ent & 0xffff;
         const int key0 = J * BLK + (st % C::SPB) * C::KT;
-        if (key0 + C::KT <= L) {
-            const char *ks = kbase + (size_t)key0 * Hkv * D * 2;
+        const bool full = key0 + C::KT <= L;
+        // Buffer resources based at this stage's first K row (clamped to row
+        // L-1 for a stage that starts at or past L) and first V^T column;
+        // each lane adds its byte offset.
+        const int krow0 = full ? key0 : min(key0, L - 1);
+        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kbase + (size_t)krow0 * Hkv * D * 2);
+        const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vbase + (size_t)key0 * 2);
 #pragma unroll
-            for (int i = 0; i < C::IK; ++i)
-                g2lds16(ks + koff[i], (lds_char *)kb + (wid * C::IK + i) * 1024);
-        } else {
-            // Short last stage: rows past L re-read row L-1 (masked later).
-#pragma unroll
-            for (int i = 0; i < C::IK; ++i) {
+        for (int i = 0; i < C::IK; ++i) {
+            uint32_t off = koff[i];
+            if (!full) {
+                // Short last stage: rows past L re-read row L-1 (masked later).
+                // krow0 <= min(key0 + r, L - 1), so the offset is not negative.
                 const int p = (wid * C::IK + i) * 64 + lane;
                 const int r = p / C::CPRK, c = (p % C::CPRK) ^ swz_k<D>(r);
-                const int key = min(key0 + r, L - 1);
-                g2lds16(K + ((size_t)key * Hkv + g) * D + c * 8, (lds_char *)kb + (wid * C::IK + i) * 1024);
+                const int rr = min(key0 + r, L - 1) - krow0;
+                off = (uint32_t)((rr * Hkv * D + c * 8) * 2);
             }
+            buf2lds16(rk, off, (lds_char *)kb + (wid * C::IK + i) * 1024);
         }
-        const char *vs = vbase + (size_t)key0 * 2;
 #pragma unroll
-        for (int i = 0; i < C::IV; ++i) g2lds16(vs + voff[i], (lds_char *)vb + (wid * C::IV + i) * 1024);
-        return true;
+        for (int i = 0; i < C::IV; ++i) buf2lds16(rv, voff[i], (lds_char *)vb + (wid * C::IV + i) * 1024);
     };
 
     // The entry is passed in (read at the top of the iteration, before the
@@ -298,16 +312,29 @@ __global__ __launch_bounds__(BLK * 4, 2) void rr_block_sparse_fa(
             fa[ks] = *reinterpret_cast<const uint4 *>(kr0 + off);
             fb[ks] = *reinterpret_cast<const uint4 *>(kr1 + off);
         };
-        rd(0);
-        rd(1);
+#pragma unroll
+        for (int ks = 0; ks < KLA; ++ks) rd(ks);
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
-            if (ks + 2 < C::NKS) rd(ks + 2);
+            if (ks + KLA < C::NKS) rd(ks + KLA);
             __builtin_amdgcn_sched_barrier(0);
             sacc[0] = mfma32x32x16(as_bf16x8(fa[ks]), qf[ks], sacc[0]);
             sacc[1] = mfma32x32x16(as_bf16x8(fb[ks]), qf[ks], sacc[1]);
             __builtin_amdgcn_sched_barrier(0);
         }
+
+        // V^T fragments of 16-key group gi (kt = gi / 2, mm = gi % 2), one per
+        // 32-row d-tile; group 0's are read before the maximum is taken and
+        // each later group's while the previous group's products run.
+        auto rdv = [&](int gi, uint4 (&a)[C::NDT]) {
+            const int voff = ((4 * (gi >> 1) + 2 * hk + (gi & 1)) ^ vsw) << 4;
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+                a[dt] = *reinterpret_cast<const uint4 *>(vb + (dt * 32 + col) * (C::KT * 2) + voff);
+        };
+        uint4 va[C::NDT], vn[C::NDT];
+        rdv(0, va);
+        __builtin_amdgcn_sched_barrier(0);
 
         float mx = -INFINITY;
         if (diag) {
@@ -337,52 +364,59 @@ __global__ __launch_bounds__(BLK * 4, 2) void rr_block_sparse_fa(
         const float nm = -m;
 
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int gi = 0; gi < 4; ++gi) {
+            const int kt = gi >> 1, mm = gi & 1;
+            uint32_t pk[4];
 #pragma unroll
-            for (int mm = 0; mm < 2; ++mm) {
-                uint32_t pk[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p0 = fast_exp2(fmaf(sacc[kt][8 * mm + 2 * e], scale2, nm));
-                    const float p1 = fast_exp2(fmaf(sacc[kt][8 * mm + 2 * e + 1], scale2, nm));
-                    pk[e] = pack_bf16x2(p0, p1);
-                    // The normaliser sums the same bf16 weights the P.V product uses.
-                    lsum = add_bf16x2(pk[e], lsum);
-                }
-                const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-                const int voff = ((4 * kt + 2 * hk + mm) ^ vsw) << 4;
-#pragma unroll
-                for (int dt = 0; dt < C::NDT; ++dt) {
-                    const uint4 a = *reinterpret_cast<const uint4 *>(vb + (dt * 32 + col) * (C::KT * 2) + voff);
-                    o[dt] = mfma32x32x16(as_bf16x8(a), pb, o[dt]);
-                }
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = fast_exp2(fmaf(sacc[kt][8 * mm + 2 * e], scale2, nm));
+                const float p1 = fast_exp2(fmaf(sacc[kt][8 * mm + 2 * e + 1], scale2, nm));
+                pk[e] = pack_bf16x2(p0, p1);
+                // The normaliser sums the same bf16 weights the P.V product uses.
+                lsum = add_bf16x2(pk[e], lsum);
             }
+            const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+            if (gi + 1 < 4) rdv(gi + 1, vn);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) o[dt] = mfma32x32x16(as_bf16x8(va[dt]), pb, o[dt]);
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) va[dt] = vn[dt];
         }
     };
 
-    // Two-stage pipeline over statically distinct LDS buffers: the copies of
-    // stage st+1 run while stage st is computed.  Each wave waits for its own
-    // copies with vmcnt, the barrier then publishes all waves' copies.
-    if (nst > 0) issue(0, stage_entry(0), Kb0, Vb0);
-    for (int st = 0; st < nst; st += 2) {
-        const int E0 = stage_entry(st), E1 = stage_entry(st + 1), E2 = stage_entry(st + 2);
-        if (st + 1 < nst && issue(st + 1, E1, Kb1, Vb1))
-            wait_vmcnt<C::LPW>();
-        else
-            wait_vmcnt<0>();
-        bar();
-        compute(st, E0, Kb0, Vb0);
-        wait_lgkm0();
-        bar();
-        if (st + 1 >= nst) break;
-        if (st + 2 < nst && issue(st + 2, E2, Kb0, Vb0))
-            wait_vmcnt<C::LPW>();
-        else
-            wait_vmcnt<0>();
-        bar();
-        compute(st + 1, E1, Kb1, Vb1);
-        wait_lgkm0();
-        bar();
+    // Stages are taken two at a time between barriers, from two pairs of
+    // buffers: while one pair is computed the copies of the next two stages
+    // fill the other.  One barrier per pair: every wave's copies of the pair
+    // have landed (vmcnt 0) and every wave has finished reading the other
+    // pair (lgkmcnt 0) before it.
+    if (nst > 0) {
+        issue(0, Kb0, Vb0);
+        issue(1, Kb1, Vb1);
+        for (int st = 0; st < nst; st += 4) {
+            {
+                const int E0 = stage_entry(st), E1 = stage_entry(st + 1);
+                wait_vmcnt<0>();
+                wait_lgkm0();
+                bar();
+                issue(st + 2, Kb2, Vb2);
+                issue(st + 3, Kb3, Vb3);
+                compute(st, E0, Kb0, Vb0);
+                compute(st + 1, E1, Kb1, Vb1);
+            }
+            if (st + 2 >= nst) break;
+            {
+                const int E2 = stage_entry(st + 2), E3 = stage_entry(st + 3);
+                wait_vmcnt<0>();
+                wait_lgkm0();
+                bar();
+                issue(st + 4, Kb0, Vb0);
+                issue(st + 5, Kb1, Vb1);
+                compute(st + 2, E2, Kb2, Vb2);
+                compute(st + 3, E3, Kb3, Vb3);
+            }
+        }
+        wait_vmcnt<0>();
     }
 
     const float tot = sum_halves(lsum);

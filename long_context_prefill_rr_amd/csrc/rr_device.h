@@ -70,6 +70,24 @@ __device__ __forceinline__ void g2lds16(const void *src, lds_char *lds_wave_base
     __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
 }
 
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
+// no swizzle): byte-addressed, offsets from a VGPR, no range clamping used.
+constexpr int kBufFlags = 0x00020000;
+
+// Buffer resource over the bytes starting at p (no range limit).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, -1, kBufFlags);
+}
+
+// 16-byte buffer -> LDS copy without registers (buffer_load_dwordx4 ... lds):
+// lane i reads rsrc base + off and writes lds_wave_base + 16*i.  Unlike the
+// flat-encoded global_load_lds, a buffer copy in flight leaves the compiler
+// able to count LDS reads in issue order, so fragment reads can run ahead of
+// their use without every wait draining all of them.
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t off, lds_char *lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, (int)off, 0, 0, 0);
+}
+
 // s_waitcnt with only the vector-memory counter constrained (<= n pending).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

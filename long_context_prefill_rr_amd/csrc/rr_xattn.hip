@@ -94,25 +94,32 @@ __global__ __launch_bounds__(512, 1) void rr_xscore(const uint16_t *__restrict__
     // instructions) and query rows 32w .. 32w+31 (4 instructions).
     const int lrow = lane >> 3;
     const int cslot = lane & 7;
+    // The copies are buffer loads: a resource based at the chunk's first key
+    // (query) row, clamped to the last stride, plus a per-lane byte offset
+    // that stays below 2^32 (at most 255 rows of S * heads * d elements).
+    const int ib = min(i0, ns - 1);
     auto issue = [&](int idx, char *ka, char *qa) {
         const int tile = idx / nkc, kc = idx - tile * nkc;
         const int t = kc / CPT, e0 = (kc - t * CPT) * kXK;
         const int j0 = tile * kXT;
+        const int jb = min(j0, ns - 1);
+        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(K + ((size_t)(jb * S + S - 1 - t) * Hkv + g) * D + e0);
+        const __amdgpu_buffer_rsrc_t rq = buf_rsrc(Q + ((size_t)(ib * S + t) * Hq + h) * D + e0);
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             const int r = 16 * wid + 8 * n + lrow;
-            const int j = min(j0 + r, ns - 1);
+            const int j = min(j0 + r, ns - 1);  // >= jb
             const int ck = cslot ^ swz_key(r);
-            const uint16_t *src = K + ((size_t)(j * S + S - 1 - t) * Hkv + g) * D + e0 + ck * 8;
-            g2lds16(src, (lds_char *)ka + (16 * wid + 8 * n) * kXRowB);
+            const uint32_t off = (uint32_t)(((j - jb) * S * Hkv * D + ck * 8) * 2);
+            buf2lds16(rk, off, (lds_char *)ka + (16 * wid + 8 * n) * kXRowB);
         }
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             const int r = 32 * wid + 8 * n + lrow;
-            const int i = min(i0 + r, ns - 1);
+            const int i = min(i0 + r, ns - 1);  // >= ib
             const int cq = cslot ^ swz_query(r);
-            const uint16_t *src = Q + ((size_t)(i * S + t) * Hq + h) * D + e0 + cq * 8;
-            g2lds16(src, (lds_char *)qa + (32 * wid + 8 * n) * kXRowB);
+            const uint32_t off = (uint32_t)(((i - ib) * S * Hq * D + cq * 8) * 2);
+            buf2lds16(rq, off, (lds_char *)qa + (32 * wid + 8 * n) * kXRowB);
         }
     };
 
@@ -220,15 +227,17 @@ __global__ __launch_bounds__(512, 1) void rr_xscore(const uint16_t *__restrict__
         else wait_vmcnt<0>();
         stored = false;
         bar();
-        if (idx + 2 < total) issue(idx + 2, kn, qn);
+        // Past the end the last chunk is copied again, into a buffer no one
+        // reads any more: every step issues the same copies.
+        issue(min(idx + 2, total - 1), kn, qn);
         compute(ka, qa);
         if ((idx + 1) % nkc == 0) {
             epilogue(idx / nkc);
             stored = true;
         }
     };
-    if (total > 0) issue(0, Ka0, Qa0);
-    if (total > 1) issue(1, Ka1, Qa1);
+    issue(0, Ka0, Qa0);
+    issue(min(1, total - 1), Ka1, Qa1);
     for (int idx = 0; idx < total; idx += 3) {
         step(idx, Ka0, Qa0, Ka2, Qa2);
         if (idx + 1 >= total) break;
@@ -236,6 +245,7 @@ __global__ __launch_bounds__(512, 1) void rr_xscore(const uint16_t *__restrict__
         if (idx + 2 >= total) break;
         step(idx + 2, Ka2, Qa2, Ka1, Qa1);
     }
+    wait_vmcnt<0>();
 
     // Row totals: the two lane halves, then the two key-half waves.
 #pragma unroll
