@@ -37,7 +37,7 @@ HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 
 CSRC = os.path.join(ROOT, "long_context_prefill_rr_amd", "csrc")
 ATTN_TRAFFIC = (os.path.join(ROOT, "profiles", "rr_block_sparse_fa_llama8b-128k_traffic.md"),
-                ["rr_attn.hip"])
+                ["rr_attn.hip", "rr_device.h"])
 EST_TRAFFIC = (os.path.join(ROOT, "profiles", "rr_estimate_select_llama8b-128k_traffic.md"),
                ["rr_estimate.hip", "rr_select.hip"])
 
