@@ -40,6 +40,8 @@ ATTN_TRAFFIC = (os.path.join(ROOT, "profiles", "rr_block_sparse_fa_llama8b-128k_
                 ["rr_attn.hip", "rr_device.h"])
 EST_TRAFFIC = (os.path.join(ROOT, "profiles", "rr_estimate_select_llama8b-128k_traffic.md"),
                ["rr_estimate.hip", "rr_select.hip"])
+MAT_TRAFFIC = (os.path.join(ROOT, "profiles", "rr_estimate_materialized_llama8b-128k_traffic.md"),
+               ["rr_estimate.hip", "rr_select.hip"])
 
 
 def measured_traffic(workload_name, spec, field):
@@ -159,6 +161,9 @@ def main():
     ap.add_argument("--quality", choices=["on", "off"], default="on",
                     help="after timing, score the kept blocks against Top-tau on the exact "
                          "block mass (rr_estimate with S = 1)")
+    ap.add_argument("--materialized", choices=["on", "off"], default="on",
+                    help="also time the materialised estimate (every stride score written to "
+                         "memory, then pooled) with the same Top-tau")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, copy q (known size) once: the reference dispatch for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -262,6 +267,42 @@ def main():
         dense_ms = de[0].elapsed_time(de[1]) / nd
         del counts_d, idx_d
         log("dense attention (every causal block): %.3f ms" % dense_ms)
+
+    # The materialised estimate: every stride score written to memory, then
+    # pooled; the same Top-tau after it.  Its bytes are what a design that
+    # stores the scores has to move.
+    materialized = None
+    if args.materialized == "on" and B // S >= 4:
+        n_sc = rr.stride_scores_count(L, Hq, Hkv, d, B, S)
+        sc = torch.empty(n_sc, dtype=torch.float32, device=dev)
+        Am = torch.empty_like(A)
+        cm, im = torch.empty_like(counts), torch.empty_like(idx)
+        for _ in range(args.warmup):
+            rr.rr_estimate_materialized(q, k, B, S, stride_scores=sc, block_scores=Am, ws=ws)
+            rr.rr_select(Am, L, B, tau, counts=cm, block_idx=im)
+        mev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for e in mev:
+            e[0].record()
+            rr.rr_estimate_materialized(q, k, B, S, stride_scores=sc, block_scores=Am, ws=ws)
+            e[1].record()
+            rr.rr_select(Am, L, B, tau, counts=cm, block_idx=im)
+            e[2].record()
+        torch.cuda.synchronize()
+        mest = np.array([e[0].elapsed_time(e[1]) for e in mev])
+        msel = np.array([e[1].elapsed_time(e[2]) for e in mev])
+        # Rows whose kept list differs from the main path's (the two sum the
+        # same probabilities in different orders; blocks at the tau boundary
+        # may fall either way).
+        diff_rows = int(((cm != counts) | (im != idx).any(dim=2)).sum().item())
+        materialized = {"estimate_ms": float(mest.mean()), "select_ms": float(msel.mean()),
+                        "ms": float(mest.mean() + msel.mean()),
+                        "stride_score_bytes": n_sc * 4, "rows_differing_from_main_path": diff_rows}
+        log("materialised estimate %.3f ms + select %.3f ms (%.1f GB of stride scores); rows "
+            "whose mask differs from the main path: %d of %d" % (
+                materialized["estimate_ms"], materialized["select_ms"], n_sc * 4 / 1e9, diff_rows,
+                Hq * nb))
+        del sc, Am, cm, im
+        torch.cuda.empty_cache()
 
     # XAttention's antidiagonal estimate on the same inputs and Top-tau, under
     # both readings of its softmax input (antidiagonal sum, antidiagonal mean).
@@ -408,6 +449,15 @@ def main():
                       + 2 * Hq * c_ * c_ * (nb * (nb + 1) // 2) * 4 + 2 * Hq * nb * nb * 4
                       + Hq * nb * nb * 4)
     est_traffic = measured_traffic(w.name, EST_TRAFFIC, "traffic_bytes_per_step")
+    if materialized is not None:
+        mt = measured_traffic(w.name, MAT_TRAFFIC, "traffic_bytes_per_step")
+        mms = materialized["ms"]
+        materialized.update({
+            "design_a_bytes": design_a_bytes,
+            "GBps_design_a_bytes": design_a_bytes / (mms * 1e-3) / 1e9,
+            "measured_bytes": mt,
+            "GBps_measured": None if mt is None else mt / (mms * 1e-3) / 1e9,
+            "hbm_frac_measured": None if mt is None else mt / (mms * 1e-3) / 1e9 / HBM_PEAK_GBPS})
     out = {
         "metric": "sparse prefill attn ms/layer + dense-equiv TFLOP/s at 128K; scoring GB/s",
         "value": dense_flops / (ms * 1e-3) / 1e12,
@@ -446,7 +496,8 @@ def main():
                     else est_traffic / (score_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                     "design_a_bytes": design_a_bytes,
                     "design_a_equivalent_hbm_frac": design_a_bytes / (score_ms * 1e-3) / 1e9
-                    / HBM_PEAK_GBPS},
+                    / HBM_PEAK_GBPS,
+                    "materialized": materialized},
         "roofline": {"kernel": "rr_block_sparse_fa (with its V transpose)", "bound": "mfma",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic(w.name, ATTN_TRAFFIC, "traffic_bytes_per_launch"),

@@ -85,6 +85,34 @@ int rr_estimate(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv, in
                 int S, float *block_scores, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * rr_estimate_materialized -- the same block scores as rr_estimate, computed
+ * by writing every stride score to memory and pooling it in a second pass
+ * (the stride-level scoring, then the stride-level softmax and aggregation,
+ * as separate steps: RRAttention summary page, Summary and Key points).  It
+ * moves far more bytes than rr_estimate (at L = 128K, 32 heads, S = 8 the
+ * scores alone are 17.2 GB, written once and read once) and exists to
+ * expose the stride scores and to measure that design; rr_estimate keeps
+ * only per-(row, block) statistics and is faster.
+ *   stride_scores out, fp32, rr_stride_scores_count(...) floats.  For head h
+ *                 and block-row I, row a (stride i = I*(B/S) + a) of that
+ *                 block-row holds the scores of strides j = 0 .. (I+1)*(B/S)-1
+ *                 at h*C*P + C*C*I*(I+1)/2 + a*(I+1)*C + j, where C = B/S and
+ *                 P = C*nb*(nb+1)/2: s = (1/sqrt(d)) * log2(e) * Q[iS + (h mod
+ *                 S)][h] . Kbar[j][g] (base-2 logits), -inf for j > i.  Rows
+ *                 a past a short last block are not written.
+ *   block_scores  out, fp32 [Hq][nb][nb], as for rr_estimate (agrees with it
+ *                 to fp32 rounding of the sums).
+ *   ws, ws_bytes  device workspace, >= rr_estimate_materialized_workspace_bytes.
+ * Supported: B/S >= 4 (S <= B/4), else RR_E_UNSUPPORTED; other shape rules as
+ * for rr_estimate.
+ */
+long long rr_stride_scores_count(int L, int Hq, int Hkv, int d, int B, int S);
+size_t rr_estimate_materialized_workspace_bytes(int L, int Hq, int Hkv, int d, int B, int S);
+int rr_estimate_materialized(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv, int d,
+                             int B, int S, float *stride_scores, float *block_scores, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/*
  * rr_select -- adaptive Top-tau per (query head, query block-row).
  * For block-row I of head h with W = sum_{J<=I} A[h][I][J]: order the blocks
  * by (score descending, block index ascending) and keep the shortest prefix

@@ -106,6 +106,38 @@ int rr_estimate(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv, in
     return run_estimate(Q, K, s, block_scores, ws, as_stream(stream));
 }
 
+long long rr_stride_scores_count(int L, int Hq, int Hkv, int d, int B, int S) {
+    if (check_shape(L, Hq, Hkv, d, B, S, true) != RR_OK || B / S < 4) return 0;
+    const Shape s = make_shape(L, Hq, Hkv, d, B, S);
+    return (long long)s.Hq * score_elems_per_head(s);
+}
+
+size_t rr_estimate_materialized_workspace_bytes(int L, int Hq, int Hkv, int d, int B, int S) {
+    if (check_shape(L, Hq, Hkv, d, B, S, true) != RR_OK || B / S < 4) return 0;
+    const Shape s = make_shape(L, Hq, Hkv, d, B, S);
+    return align_up((size_t)3 * s.Hkv * s.ns * s.d * 2);  // the pooled-key planes
+}
+
+int rr_estimate_materialized(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv, int d,
+                             int B, int S, float *stride_scores, float *block_scores, void *ws,
+                             size_t ws_bytes, void *stream) {
+    if (!Q || !K || !stride_scores || !block_scores || !ws) return RR_E_NULL;
+    int rc = check_shape(L, Hq, Hkv, d, B, S, true);
+    if (rc != RR_OK) return rc;
+    if (B / S < 4) return RR_E_UNSUPPORTED;
+    const Shape s = make_shape(L, Hq, Hkv, d, B, S);
+    if (ws_bytes < rr_estimate_materialized_workspace_bytes(L, Hq, Hkv, d, B, S)) return RR_E_WORKSPACE;
+    EstimateWs w;
+    w.kplanes = (uint16_t *)ws;
+    w.stats = nullptr;
+    w.rowstat = nullptr;
+    hipStream_t st = as_stream(stream);
+    if (launch_pool_k(K, s, w.kplanes, st) != hipSuccess) return RR_E_HIP;
+    if (launch_score_store(Q, s, w, stride_scores, st) != hipSuccess) return RR_E_HIP;
+    if (launch_pool_scores(s, stride_scores, block_scores, st) != hipSuccess) return RR_E_HIP;
+    return RR_OK;
+}
+
 int rr_select(const float *block_scores, int Hq, int L, int B, float tau, int32_t *counts,
               int32_t *block_idx, void *stream) {
     if (!block_scores || !counts || !block_idx) return RR_E_NULL;

@@ -111,8 +111,10 @@ __device__ __forceinline__ float sum_halves(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// A 64-row block makes a 4-wave work-group that fits once per CU (LDS): one
+// wave per SIMD.
 template <int D, int BLK, bool OUT_F32>
-__global__ __launch_bounds__(BLK * 4, 2) void rr_block_sparse_fa(
+__global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_fa(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ Vt,
     int L, int Lp, int Hq, int Hkv, int nb, int nq, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ block_idx, void *__restrict__ O, float scale2) {

@@ -5,6 +5,15 @@
 //                           (row, key-block) running max / sum-of-exponentials
 //   rr_stride_softmax_pool  causal row softmax folded into B x B block sums
 //
+// and the materialised variant of the same estimate, which writes every
+// stride score to memory and pools it in a second pass:
+//
+//   rr_score<..., STORE>           the same products; the scaled scores of
+//                                  every (row, stride j <= block end) stored
+//   rr_stride_softmax_pool_scores  reads each row of scores once: per-block
+//                                  max / sum in LDS, the row softmax, then
+//                                  the block sums
+//
 // Method: one query per stride of S tokens, offset h mod S rotating with the
 // query head, scored against the mean key of every earlier-or-equal stride,
 // softmax over strides, probabilities summed per block (RRAttention summary
@@ -79,6 +88,13 @@ __device__ __forceinline__ long long packed_offset(int C, int I, int a, int J) {
     return (long long)C * I * (I + 1) / 2 + (long long)J * C + a;
 }
 
+// Offset of stride score (row (I, a), stride j) in a head's stored scores:
+// block-row I owns c rows of (I+1)c strides, row-major, after the c^2 I(I+1)/2
+// entries of block-rows 0 .. I-1.
+__device__ __forceinline__ long long score_offset(int C, int I, int a, int j) {
+    return (long long)C * C * I * (I + 1) / 2 + (long long)a * (I + 1) * C + j;
+}
+
 // ---------------------------------------------------------------------------
 // rr_score: one work-group per (group of R consecutive query block-rows
 // I0 .. I0+R-1, kv-head g, chunk of up to 256 sampled rows).  The rows are
@@ -99,13 +115,18 @@ __device__ __forceinline__ long long packed_offset(int C, int I, int a, int J) {
 // ---------------------------------------------------------------------------
 constexpr int kScoreRows = 256;
 
-template <int D, int C>
+// With STORE set, the statistics are replaced by the scores themselves:
+// scores[h][c^2 I(I+1)/2 + a (I+1)c + j] = s(row (I, a), stride j) in log2
+// units, -inf for j > i, for every j < (I+1)c (layout of score_offset).
+template <int D, int C, bool STORE = false>
 __global__ __launch_bounds__(256) void rr_score(const uint16_t *__restrict__ Q,
                                                 const uint16_t *__restrict__ Kp, int Hq, int Hkv,
                                                 int S, int nb, int ns, int G, int R, int nchunks,
                                                 long long P, float scale2,
                                                 float2 *__restrict__ stats,
-                                                float2 *__restrict__ rowstat) {
+                                                float2 *__restrict__ rowstat,
+                                                float *__restrict__ scores = nullptr) {
+    static_assert(!STORE || C >= 4, "stored scores are written four strides at a time");
     constexpr int KS = D / 32;
     constexpr int CPR = D / 8;                 // 16-byte chunks per Q row
     constexpr int NSUB = C >= 16 ? C / 16 : 1;
@@ -235,7 +256,20 @@ __global__ __launch_bounds__(256) void rr_score(const uint16_t *__restrict__ Q,
                 for (int e = 0; e < 4; ++e)
                     if (j0 + lg * 4 + e > row_i[rt]) acc[e] = -INFINITY;
             }
-            if constexpr (C >= 16) {
+            if constexpr (STORE) {
+                // Strides j0 + 4 lg .. + 3 of this lane's row, if they lie in
+                // the row's packed range j < (I+1)c (C >= 4: all four or none).
+                const int jj = j0 + lg * 4;
+                if (row_i[rt] >= 0) {
+                    const int I = row_i[rt] / C, a = row_i[rt] - I * C;
+                    if (jj < (I + 1) * C) {
+                        const float4 v = make_float4(acc[0] * scale2, acc[1] * scale2, acc[2] * scale2,
+                                                     acc[3] * scale2);
+                        *reinterpret_cast<float4 *>(scores + (size_t)row_h[rt] * (size_t)(C * P) +
+                                                    score_offset(C, I, a, jj)) = v;
+                    }
+                }
+            } else if constexpr (C >= 16) {
                 const int J = j0 / C;
                 const int sub = (j0 % C) / 16;
                 float mr = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
@@ -298,6 +332,7 @@ __global__ __launch_bounds__(256) void rr_score(const uint16_t *__restrict__ Q,
         process(t + 1, kB);
     }
 
+    if constexpr (STORE) return;
     // Per-row totals: butterfly over the four lane groups, then across waves.
 #pragma unroll
     for (int rt = 0; rt < MT; ++rt) {
@@ -378,6 +413,86 @@ __global__ __launch_bounds__(256) void rr_stride_softmax_pool(const float2 *__re
 }
 
 // ---------------------------------------------------------------------------
+// rr_stride_softmax_pool_scores: the pooling of the materialised variant.
+// One work-group per (block-row I, query head h); the block-row's rows are
+// taken one after the other.  For row a, lane t reads strides 4t .. 4t+3 of
+// each 1024-stride pass (float4, coalesced): the C/4 lanes of one block give
+// its (max, sum of 2^(s - max)) by a butterfly and park it in LDS, and the
+// lanes' running (max, sum) give the row's (M_a, Z_a) through a work-group
+// reduction (the loads of four passes are issued before any is used, for
+// more bytes in flight).  Then A[J] += z_J 2^(m_J - M_a) / Z_a for every
+// J <= I, in LDS.
+// Each score is read once; all sums run in a fixed order.
+// ---------------------------------------------------------------------------
+constexpr int kPoolMaxNb = 4096;
+
+template <int C>
+__global__ __launch_bounds__(256) void rr_stride_softmax_pool_scores(const float *__restrict__ scores,
+                                                                     int nb, int ns, long long SP,
+                                                                     float *__restrict__ A) {
+    static_assert(C >= 4 && C <= 128, "blocks of 4 .. 128 strides");
+    constexpr int LPB = C / 4;  // lanes per block
+    __shared__ float2 bst[kPoolMaxNb];
+    __shared__ float acc[kPoolMaxNb];
+    __shared__ float2 red[4];
+    const int I = blockIdx.x, h = blockIdx.y;
+    const int cI = min(C, ns - I * C);
+    const int span = (I + 1) * C;
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+    for (int J = tid; J <= I; J += 256) acc[J] = 0.f;
+    const float *rowbase = scores + (size_t)h * SP + (size_t)C * C * I * (I + 1) / 2;
+    for (int a = 0; a < cI; ++a) {
+        const float4 *row = reinterpret_cast<const float4 *>(rowbase + (size_t)a * span);
+        float rm = -INFINITY, rz = 0.f;
+        const int nq = span / 4;
+        // Four 1024-stride passes per round: their loads are issued together.
+        for (int q0 = 0; q0 < nq; q0 += 4 * 256) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int q = q0 + u * 256 + tid;
+                v[u] = q < nq ? row[q] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int q = q0 + u * 256 + tid;
+                float m = fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)), z = 0.f;
+                if (m != -INFINITY)
+                    z = fast_exp2(v[u].x - m) + fast_exp2(v[u].y - m) + fast_exp2(v[u].z - m) +
+                        fast_exp2(v[u].w - m);
+#pragma unroll
+                for (int o = 1; o < LPB; o <<= 1) {
+                    const float m2 = xor_lane(m, o), z2 = xor_lane(z, o);
+                    merge_max_sum(m, z, m2, z2);
+                }
+                if (q < nq && (lane & (LPB - 1)) == 0) bst[q / LPB] = make_float2(m, z);
+                merge_max_sum(rm, rz, m, z);
+            }
+        }
+        // Row totals: butterfly within each wave (lanes of one block already
+        // agree), then the four waves in order.
+#pragma unroll
+        for (int o = LPB; o < kWave; o <<= 1) {
+            const float m2 = xor_lane(rm, o), z2 = xor_lane(rz, o);
+            merge_max_sum(rm, rz, m2, z2);
+        }
+        if (lane == 0) red[wid] = make_float2(rm, rz);
+        __syncthreads();
+        float M = -INFINITY, Z = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) merge_max_sum(M, Z, red[w].x, red[w].y);
+        const float invZ = 1.f / Z;
+        for (int J = tid; J <= I; J += 256) {
+            const float2 b = bst[J];
+            if (b.x != -INFINITY) acc[J] += b.y * fast_exp2(b.x - M) * invZ;
+        }
+        __syncthreads();
+    }
+    float *out = A + ((size_t)h * nb + I) * nb;
+    for (int J = tid; J < nb; J += 256) out[J] = (J <= I) ? acc[J] : 0.f;
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_pool_k(const uint16_t *K, const Shape &s, uint16_t *kplanes, hipStream_t st) {
@@ -423,6 +538,62 @@ hipError_t launch_score(const uint16_t *Q, const Shape &s, const EstimateWs &w, 
         launch_score_d<128>(Q, s, w, st);
     else
         launch_score_d<64>(Q, s, w, st);
+    return hipGetLastError();
+}
+
+template <int D>
+static void launch_score_store_d(const uint16_t *Q, const Shape &s, const EstimateWs &w, float *scores,
+                                 hipStream_t st) {
+    const int GC = s.G * s.c;
+    const int R = std::max(1, std::min(s.nb, kScoreRows / GC));
+    const int nchunks = (R * GC + kScoreRows - 1) / kScoreRows;
+    const int ngrp = (s.nb + R - 1) / R;
+    const dim3 grid((unsigned)(ngrp * s.Hkv * nchunks));
+    const float scale2 = kLog2e / sqrtf((float)D);
+#define RR_SCORE_STORE_CASE(CC)                                                                \
+    case CC:                                                                                   \
+        hipLaunchKernelGGL((rr_score<D, CC, true>), grid, dim3(256), 0, st, Q, w.kplanes, s.Hq,  \
+                           s.Hkv, s.S, s.nb, s.ns, s.G, R, nchunks, s.P, scale2, (float2 *)nullptr, \
+                           (float2 *)nullptr, scores);                                         \
+        break;
+    switch (s.c) {
+        RR_SCORE_STORE_CASE(4)
+        RR_SCORE_STORE_CASE(8)
+        RR_SCORE_STORE_CASE(16)
+        RR_SCORE_STORE_CASE(32)
+        RR_SCORE_STORE_CASE(64)
+        RR_SCORE_STORE_CASE(128)
+        default: break;
+    }
+#undef RR_SCORE_STORE_CASE
+}
+
+hipError_t launch_score_store(const uint16_t *Q, const Shape &s, const EstimateWs &w, float *scores,
+                              hipStream_t st) {
+    if (s.d == 128)
+        launch_score_store_d<128>(Q, s, w, scores, st);
+    else
+        launch_score_store_d<64>(Q, s, w, scores, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_scores(const Shape &s, const float *scores, float *A, hipStream_t st) {
+    const long long SP = score_elems_per_head(s);
+#define RR_POOL_SCORES_CASE(CC)                                                                \
+    case CC:                                                                                   \
+        hipLaunchKernelGGL(rr_stride_softmax_pool_scores<CC>, dim3(s.nb, s.Hq), dim3(256), 0, st, \
+                           scores, s.nb, s.ns, SP, A);                                         \
+        break;
+    switch (s.c) {
+        RR_POOL_SCORES_CASE(4)
+        RR_POOL_SCORES_CASE(8)
+        RR_POOL_SCORES_CASE(16)
+        RR_POOL_SCORES_CASE(32)
+        RR_POOL_SCORES_CASE(64)
+        RR_POOL_SCORES_CASE(128)
+        default: break;
+    }
+#undef RR_POOL_SCORES_CASE
     return hipGetLastError();
 }
 

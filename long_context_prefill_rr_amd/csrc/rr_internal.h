@@ -59,6 +59,10 @@ inline EstimateWs carve_estimate(const Shape &s, void *ws) {
     return w;
 }
 
+// Stored stride scores of the materialised estimate: per head, block-row I
+// owns c rows of (I+1)c strides, i.e. c * P floats in all.
+inline long long score_elems_per_head(const Shape &s) { return (long long)s.c * s.P; }
+
 // Attention workspace: V transposed to [Hkv][d][nb*B] (zero-padded tail).
 inline size_t attn_ws_bytes(const Shape &s) { return align_up((size_t)s.Hkv * s.d * s.nb * s.B * 2); }
 
@@ -66,6 +70,9 @@ inline size_t attn_ws_bytes(const Shape &s) { return align_up((size_t)s.Hkv * s.
 hipError_t launch_pool_k(const uint16_t *K, const Shape &s, uint16_t *kplanes, hipStream_t st);
 hipError_t launch_score(const uint16_t *Q, const Shape &s, const EstimateWs &w, hipStream_t st);
 hipError_t launch_softmax_pool(const Shape &s, const EstimateWs &w, float *A, hipStream_t st);
+hipError_t launch_score_store(const uint16_t *Q, const Shape &s, const EstimateWs &w, float *scores,
+                              hipStream_t st);
+hipError_t launch_pool_scores(const Shape &s, const float *scores, float *A, hipStream_t st);
 hipError_t launch_topk_tau(const float *A, const Shape &s, float tau, int32_t *counts,
                            int32_t *block_idx, hipStream_t st);
 hipError_t launch_transpose_v(const uint16_t *V, const Shape &s, uint16_t *Vt, hipStream_t st);

@@ -66,8 +66,14 @@ def _load():
         lib.rr_rescue_workspace_bytes.restype = z
         lib.rr_rescue_estimate.argtypes = [P, P, i, i, i, i, i, P, P, z, P]
         lib.rr_merge_masks.argtypes = [P, P, P, P, i, i, i, P, P, P]
+        lib.rr_stride_scores_count.argtypes = [i, i, i, i, i, i]
+        lib.rr_stride_scores_count.restype = ctypes.c_longlong
+        lib.rr_estimate_materialized_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        lib.rr_estimate_materialized_workspace_bytes.restype = z
+        lib.rr_estimate_materialized.argtypes = [P, P, i, i, i, i, i, i, P, P, P, z, P]
         for name in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill", "rr_mask_quality",
-                     "rr_xattn_estimate", "rr_rescue_estimate", "rr_merge_masks"):
+                     "rr_xattn_estimate", "rr_rescue_estimate", "rr_merge_masks",
+                     "rr_estimate_materialized"):
             getattr(lib, name).restype = i
         _lib = lib
     return _lib
@@ -131,6 +137,38 @@ def rr_estimate(q, k, B, S, block_scores=None, ws=None, stream=None):
                          _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream_ptr(stream))
     _check(rc, "rr_estimate")
     return block_scores
+
+
+def stride_scores_count(L, Hq, Hkv, d, B, S):
+    """Floats of rr_estimate_materialized's stride-score buffer (0: unsupported shape)."""
+    return _load().rr_stride_scores_count(L, Hq, Hkv, d, B, S)
+
+
+def rr_estimate_materialized(q, k, B, S, stride_scores=None, block_scores=None, ws=None,
+                             stream=None):
+    """(stride_scores, block_scores): every stride score written to memory
+    (packed layout of include/rr.h, base-2 logits, -inf above the diagonal),
+    then pooled; block_scores as for rr_estimate."""
+    L, Hq, d = q.shape
+    Hkv = k.shape[1]
+    nb = -(-L // B)
+    lib = _load()
+    n = lib.rr_stride_scores_count(L, Hq, Hkv, d, B, S)
+    if stride_scores is None:
+        stride_scores = torch.empty(max(n, 1), dtype=torch.float32, device=q.device)
+    if block_scores is None:
+        block_scores = torch.empty((Hq, nb, nb), dtype=torch.float32, device=q.device)
+    ws = _workspace(lib.rr_estimate_materialized_workspace_bytes(L, Hq, Hkv, d, B, S), q.device, ws)
+    if stride_scores.numel() < n:
+        raise ValueError("stride_scores holds %d floats, %d needed" % (stride_scores.numel(), n))
+    rc = lib.rr_estimate_materialized(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), L,
+                                      Hq, Hkv, d, B, S,
+                                      _dev(stride_scores, "stride_scores", torch.float32),
+                                      _dev(block_scores, "block_scores", torch.float32),
+                                      _dev(ws, "ws"), ws.numel() * ws.element_size(),
+                                      _stream_ptr(stream))
+    _check(rc, "rr_estimate_materialized")
+    return stride_scores, block_scores
 
 
 def rr_xattn_estimate(q, k, B, S, block_scores=None, ws=None, stream=None, average=False):

@@ -45,6 +45,7 @@ def _load():
         i = ctypes.c_int
         lib.rro_pool_keys.argtypes = [P, i, i, i, i, P]
         lib.rro_stride_scores.argtypes = [P, P, i, i, i, i, i, i, i, P]
+        lib.rro_stride_score_rows.argtypes = [P, P, i, i, i, i, i, P, i, P]
         lib.rro_block_scores.argtypes = [P, P, i, i, i, i, i, i, P, i, P]
         lib.rro_xattn_stride_scores.argtypes = [P, P, i, i, i, i, i, i, i, i, P]
         lib.rro_xattn_block_scores.argtypes = [P, P, i, i, i, i, i, i, i, P, i, P]
@@ -53,7 +54,7 @@ def _load():
         lib.rro_attention.argtypes = [P, P, P, i, i, i, i, i, P, P, i, P]
         lib.rro_set_threads.argtypes = [i]
         lib.rro_get_threads.restype = i
-        for f in ("rro_pool_keys", "rro_stride_scores", "rro_block_scores", "rro_select",
+        for f in ("rro_pool_keys", "rro_stride_scores", "rro_stride_score_rows", "rro_block_scores", "rro_select",
                   "rro_xattn_stride_scores", "rro_xattn_block_scores", "rro_rescue_scores",
                   "rro_attention"):
             getattr(lib, f).restype = i
@@ -101,6 +102,20 @@ def stride_scores(q, k, S, h, i):
     _check(_load().rro_stride_scores(_ptr(q), _ptr(k), L, Hq, Hkv, d, S, h, i, _ptr(out)),
            "stride_scores")
     return out
+
+
+def stride_score_rows(q, k, S, rows):
+    """E2 for many stride rows: rows is a list of (h, i); returns the list of
+    score arrays s[0..i] (same values as stride_scores, pooled keys formed once)."""
+    q, k = _u16(q), _u16(k)
+    L, Hq, d = q.shape
+    Hkv = k.shape[1]
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
+    lens = rows[:, 1].astype(np.int64) + 1
+    out = np.empty(int(lens.sum()), dtype=np.float64)
+    _check(_load().rro_stride_score_rows(_ptr(q), _ptr(k), L, Hq, Hkv, d, S, _ptr(rows),
+                                         rows.shape[0], _ptr(out)), "stride_score_rows")
+    return np.split(out, np.cumsum(lens)[:-1])
 
 
 def block_scores(q, k, B, S, rows=None):

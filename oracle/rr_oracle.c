@@ -204,6 +204,42 @@ int rro_stride_scores(const uint16_t *Q, const uint16_t *K, int L, int Hq, int H
 }
 
 /*
+ * E2 for a list of stride rows, for tests: rows holds nrows pairs (h, i);
+ * the scores s[0..i] of row r are written to out + sum_{r' < r} (i_r' + 1).
+ * Same arithmetic as rro_stride_scores; the pooled keys are formed once.
+ */
+int rro_stride_score_rows(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv,
+                          int d, int S, const int32_t *rows, int nrows, double *out)
+{
+    if (!Q || !K || !rows || !out || nrows < 0 || !shape_ok(L, Hq, Hkv, d, S, S)) return RRO_E_ARG;
+    int ns = L / S, G = Hq / Hkv;
+    size_t *off = (size_t *)malloc(sizeof(size_t) * (size_t)(nrows + 1));
+    if (!off) return RRO_E_NOMEM;
+    off[0] = 0;
+    for (int r = 0; r < nrows; ++r) {
+        int h = rows[2 * r], i = rows[2 * r + 1];
+        if (h < 0 || h >= Hq || i < 0 || i >= ns) {
+            free(off);
+            return RRO_E_ARG;
+        }
+        off[r + 1] = off[r] + (size_t)i + 1;
+    }
+    double *KbarT = pooled_keys_transposed(K, L, Hkv, d, S);
+    if (!KbarT) {
+        free(off);
+        return RRO_E_NOMEM;
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; ++r) {
+        int h = rows[2 * r], i = rows[2 * r + 1];
+        stride_scores(Q, KbarT + (size_t)(h / G) * d * ns, ns, Hq, d, S, h, i, out + off[r]);
+    }
+    free(KbarT);
+    free(off);
+    return RRO_OK;
+}
+
+/*
  * E1-E4 -- block scores for a list of (head, query block-row) pairs
  * [RR-dig step 4 and RR-abs "stride-level aggregation"; B from RR-sum
  * "Key points"].  With c = B/S strides per block and c_I strides in block I

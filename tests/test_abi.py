@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill", "rr_mask_quality",
-              "rr_xattn_estimate", "rr_rescue_estimate", "rr_merge_masks"):
+              "rr_xattn_estimate", "rr_rescue_estimate", "rr_merge_masks", "rr_estimate_materialized"):
         assert n in names
 
 
@@ -159,3 +159,26 @@ def test_rescue_and_merge_validation(lib):
     assert m(L=0) == RR_E_SHAPE
     assert m(L=128 * 4097) == RR_E_UNSUPPORTED
 
+
+
+def test_materialized_estimate_validation(lib):
+    # Packed stride scores: Hq * c * P floats, P = c * nb(nb+1)/2.
+    L, Hq, Hkv, d, B, S = 1216, 8, 2, 128, 128, 8
+    c, nb = B // S, -(-L // B)
+    assert lib.rr_stride_scores_count(L, Hq, Hkv, d, B, S) == Hq * c * c * nb * (nb + 1) // 2
+    assert lib.rr_stride_scores_count(L, Hq, Hkv, d, B, 64) == 0         # B/S = 2 < 4
+    assert lib.rr_stride_scores_count(1004, Hq, Hkv, d, B, S) == 0       # L % S
+    ns = L // S
+    assert lib.rr_estimate_materialized_workspace_bytes(L, Hq, Hkv, d, B, S) >= 3 * Hkv * ns * d * 2
+    assert lib.rr_estimate_materialized_workspace_bytes(L, 6, 4, d, B, S) == 0
+
+    def e(L=1024, S=8, B=128, Q=FAKE, sc=FAKE, ws_bytes=1 << 40, d=128):
+        return lib.rr_estimate_materialized(Q, FAKE, L, 8, 2, d, B, S, sc, FAKE, FAKE, ws_bytes, None)
+    assert e(Q=None) == RR_E_NULL
+    assert e(sc=None) == RR_E_NULL
+    assert e(S=64) == RR_E_UNSUPPORTED      # B/S = 2
+    assert e(S=128) == RR_E_UNSUPPORTED     # B/S = 1
+    assert e(L=1004) == RR_E_SHAPE          # L % S
+    assert e(d=96) == RR_E_UNSUPPORTED
+    assert e(ws_bytes=16) == RR_E_WORKSPACE
+    assert e(L=128 * 4097) == RR_E_UNSUPPORTED

@@ -180,3 +180,14 @@ def test_oracle_regression_fixture():
     assert cnt.tolist() == fx["counts"]
     np.testing.assert_allclose(A[0, 7], fx["A_head0_row7"], rtol=1e-12)
     np.testing.assert_allclose(A[5, 3, :4], fx["A_head5_row3"], rtol=1e-12)
+
+
+def test_batched_stride_scores_equal_single_rows():
+    # The batched E2 call forms the pooled keys once and must return exactly
+    # the single-row values (same arithmetic, same order).
+    w, g = small_workload(kind="llama", L=512, Hq=4, Hkv=2, d=32, B=64, S=8, seed=5)
+    rows = [(0, 0), (3, 63), (1, 17), (2, 40), (0, 63)]
+    got = oracle.stride_score_rows(g["q"], g["k"], 8, rows)
+    for (h, i), s in zip(rows, got):
+        assert s.shape == (i + 1,)
+        assert np.array_equal(s, oracle.stride_scores(g["q"], g["k"], 8, h, i))
