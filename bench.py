@@ -40,6 +40,8 @@ ATTN_TRAFFIC = (os.path.join(ROOT, "profiles", "rr_block_sparse_fa_llama8b-128k_
                 ["rr_attn.hip", "rr_device.h"])
 EST_TRAFFIC = (os.path.join(ROOT, "profiles", "rr_estimate_select_llama8b-128k_traffic.md"),
                ["rr_estimate.hip", "rr_select.hip"])
+MFMA_BUSY = (os.path.join(ROOT, "profiles", "rr_block_sparse_fa_llama8b-128k_mfma_busy.md"),
+             ["rr_attn.hip", "rr_device.h"])
 MAT_TRAFFIC = (os.path.join(ROOT, "profiles", "rr_estimate_materialized_llama8b-128k_traffic.md"),
                ["rr_estimate.hip", "rr_select.hip"])
 
@@ -501,7 +503,11 @@ def main():
         "roofline": {"kernel": "rr_block_sparse_fa (with its V transpose)", "bound": "mfma",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic(w.name, ATTN_TRAFFIC, "traffic_bytes_per_launch"),
-                     "flops_per_launch": flops_kept},
+                     "flops_per_launch": flops_kept,
+                     # rocprof counters of this kernel (committed summary, same sources):
+                     # matrix-unit busy cycles over all SIMD cycles, and the clock it ran at.
+                     "mfma_busy_counter": measured_traffic(w.name, MFMA_BUSY, "mfma_busy_frac"),
+                     "clock_ghz_under_load": measured_traffic(w.name, MFMA_BUSY, "clock_ghz")},
     }
     if args.cpu_baseline == "on":
         log("cpu baseline (oracle) on a sample ...")
