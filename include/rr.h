@@ -23,6 +23,8 @@
  *    `stream` (a hipStream_t passed as void*, NULL = the null stream) and the
  *    call returns as soon as it is enqueued.  Nothing outside the given
  *    buffers is written.  Results are ready when the stream reaches them.
+ *    Only kernels are enqueued (no memset, copy or host callback), so a call
+ *    may be captured into a HIP graph and replayed on the same buffers.
  *  - Errors: argument checks run on the host before any launch and return a
  *    nonzero rr_status with no work enqueued; RR_E_HIP reports a failed
  *    launch (outputs are then undefined).  The library keeps no state and
