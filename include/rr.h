@@ -17,7 +17,7 @@
  *  - nb = ceil(L / B) key/query blocks; ns = L / S strides.
  *  - Supported shapes: d in {64, 128}; B in {64, 128}; S a power of two with
  *    S <= B; L % S == 0 (L % B may be nonzero: the last block is short);
- *    Hq % Hkv == 0; nb <= 4096.
+ *    Hq % Hkv == 0; Hq <= 1024; nb <= 4096.
  *  - The caller owns every buffer (inputs, outputs and workspace).  The
  *    library never allocates, frees or synchronises; all work is enqueued on
  *    `stream` (a hipStream_t passed as void*, NULL = the null stream) and the
@@ -46,7 +46,7 @@ typedef enum {
     RR_E_SHAPE = 2,       /* non-positive size, Hq % Hkv, B % S or L % S nonzero, S > B */
     RR_E_TAU = 3,         /* tau is NaN or outside (0, 1] */
     RR_E_WORKSPACE = 4,   /* ws_bytes below the required workspace size */
-    RR_E_UNSUPPORTED = 5, /* d, B or S outside the compiled instantiations, nb too large */
+    RR_E_UNSUPPORTED = 5, /* d, B or S outside the compiled instantiations, nb or Hq too large */
     RR_E_HIP = 6          /* a HIP launch failed */
 } rr_status;
 

@@ -13,12 +13,16 @@ using namespace rr;
 namespace {
 
 constexpr int kMaxBlocks = 4096;  // longest Top-tau row the selection kernel sorts
+constexpr int kMaxHeads = 1024;   // query heads per call
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int check_shape(int L, int Hq, int Hkv, int d, int B, int S, bool need_S) {
     if (L <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || B <= 0) return RR_E_SHAPE;
     if (Hq % Hkv != 0) return RR_E_SHAPE;
+    // Per-lane copy offsets inside one tile are 32-bit (a few hundred rows of
+    // S * heads * d elements): bound the head count.
+    if (Hq > kMaxHeads) return RR_E_UNSUPPORTED;
     if (need_S) {
         if (S <= 0 || S > B || B % S != 0 || L % S != 0) return RR_E_SHAPE;
         if (!is_pow2(S)) return RR_E_UNSUPPORTED;
@@ -142,6 +146,7 @@ int rr_select(const float *block_scores, int Hq, int L, int B, float tau, int32_
               int32_t *block_idx, void *stream) {
     if (!block_scores || !counts || !block_idx) return RR_E_NULL;
     if (L <= 0 || Hq <= 0 || B <= 0) return RR_E_SHAPE;
+    if (Hq > kMaxHeads) return RR_E_UNSUPPORTED;
     if ((L + B - 1) / B > kMaxBlocks) return RR_E_UNSUPPORTED;
     int rc = check_tau(tau);
     if (rc != RR_OK) return rc;
@@ -189,6 +194,7 @@ int rr_mask_quality(const int32_t *counts, const int32_t *block_idx, const int32
     if (!counts || !block_idx || !ref_counts || !ref_block_idx || !mass || !rows || !totals)
         return RR_E_NULL;
     if (L <= 0 || Hq <= 0 || B <= 0) return RR_E_SHAPE;
+    if (Hq > kMaxHeads) return RR_E_UNSUPPORTED;
     const int nb = (L + B - 1) / B;
     if (nb > kMaxBlocks) return RR_E_UNSUPPORTED;
     if (launch_mask_quality(counts, block_idx, ref_counts, ref_block_idx, mass, Hq, nb, rows,
@@ -237,6 +243,7 @@ int rr_merge_masks(const int32_t *counts_a, const int32_t *block_idx_a, const in
     if (!counts_a || !block_idx_a || !counts_b || !block_idx_b || !counts || !block_idx)
         return RR_E_NULL;
     if (L <= 0 || Hq <= 0 || B <= 0) return RR_E_SHAPE;
+    if (Hq > kMaxHeads) return RR_E_UNSUPPORTED;
     const int nb = (L + B - 1) / B;
     if (nb > kMaxBlocks) return RR_E_UNSUPPORTED;
     if (launch_merge_lists(counts_a, block_idx_a, counts_b, block_idx_b, Hq, nb, counts,

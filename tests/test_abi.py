@@ -70,6 +70,8 @@ def test_estimate_validation(lib):
     assert _est(lib, B=256, S=8) == RR_E_UNSUPPORTED
     assert _est(lib, ws_bytes=16) == RR_E_WORKSPACE
     assert _est(lib, L=128 * 4097) == RR_E_UNSUPPORTED
+    assert _est(lib, Hq=2048, Hkv=2) == RR_E_UNSUPPORTED   # more than 1024 query heads
+    assert lib.rr_select(FAKE, 2048, 1024, 128, ctypes.c_float(0.9), FAKE, FAKE, None) == RR_E_UNSUPPORTED
 
 
 def test_workspace_sizes(lib):
