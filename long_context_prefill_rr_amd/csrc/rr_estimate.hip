@@ -1,8 +1,11 @@
 // rr_estimate.hip -- the estimation kernels of the round-robin block scores.
 //
 //   rr_pool_k               K -> stride-mean keys, split into three bf16 planes
-//   rr_score                sampled queries x pooled keys on bf16 MFMA; per
-//                           (row, key-block) running max / sum-of-exponentials
+//   rr_score32              sampled queries x pooled keys on bf16 MFMA (32 x 32
+//                           tiles, blocks of 4 to 16 strides); per (row,
+//                           key-block) max / sum-of-exponentials
+//   rr_score                the same with 16 x 16 tiles, for the other block
+//                           sizes (1, 2, 32, 64, 128 strides)
 //   rr_stride_softmax_pool  causal row softmax folded into B x B block sums
 //
 // and the materialised variant of the same estimate, which writes every
@@ -359,6 +362,215 @@ __global__ __launch_bounds__(256) void rr_score(const uint16_t *__restrict__ Q,
 }
 
 // ---------------------------------------------------------------------------
+// rr_score32: rr_score's work split, rows and outputs for blocks of 4, 8 or
+// 16 strides, with 32 x 32 tiles on v_mfma_f32_32x32x16_bf16.  The pooled-key
+// rows fed to the matrix unit are permuted so that accumulator register e of
+// lane (row q, half) holds stride 16*half + e of the 32-stride unit: a lane
+// owns whole key blocks of its row, and each block's max and sum of
+// exponentials are taken in registers with no cross-lane step (the 16-stride
+// tiles of rr_score spread a block over four lanes).  The waves take units
+// wid, wid+4, ...; a unit's pooled-key fragments (3 planes x d/16 steps) stay
+// in registers across the work-group's row tiles, and during the last row
+// tile each step's fragments are reloaded with the next unit's once that
+// step's products are issued.
+// ---------------------------------------------------------------------------
+template <int D, int C>
+__global__ __launch_bounds__(256, 2) void rr_score32(const uint16_t *__restrict__ Q,
+                                                     const uint16_t *__restrict__ Kp, int Hq, int Hkv,
+                                                     int S, int nb, int ns, int G, int R, int nchunks,
+                                                     long long P, float scale2,
+                                                     float2 *__restrict__ stats,
+                                                     float2 *__restrict__ rowstat) {
+    static_assert(C == 4 || C == 8 || C == 16, "blocks of 4, 8 or 16 strides");
+    constexpr int NKS = D / 16;                // 16-wide contraction steps
+    constexpr int CPR = D / 8;                 // 16-byte chunks per Q row
+    constexpr int MT = kScoreRows / 32;        // row tiles per work-group
+    constexpr int BPL = 16 / C;                // key blocks per lane per unit
+    __shared__ __attribute__((aligned(16))) uint16_t qs[kScoreRows * D];
+    __shared__ float2 red[4][kScoreRows];
+
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int q = lane & 31, hk = lane >> 5;
+
+    // Decode: block-row groups in descending order (long rows first).
+    int b = blockIdx.x;
+    const int chunk = b % nchunks;
+    b /= nchunks;
+    const int g = b % Hkv;
+    const int ngrp = (nb + R - 1) / R;
+    const int I0 = (ngrp - 1 - b / Hkv) * R;
+    const int GC = G * C;
+    const int rows_total = min(R, nb - I0) * GC;
+    const int row0 = chunk * kScoreRows;
+    const int rows_here = min(kScoreRows, rows_total - row0);
+    const int NT = (rows_here + 31) >> 5;
+    const int Itop = min(I0 + R, nb) - 1;
+    const size_t plane = (size_t)Hkv * ns * D;
+    const uint16_t *kb = Kp + (size_t)g * ns * D;
+
+    // Row f (0..rows_here) -> (block-row, head, stride); -1 stride if invalid.
+    auto row_of = [&](int f, int &I, int &h, int &i) {
+        const int ff = row0 + f;
+        I = I0 + ff / GC;
+        const int rem = ff % GC, hh = rem / C, a = rem % C;
+        h = g * G + hh;
+        const int cI = min(C, ns - I * C);
+        i = (f < rows_here && a < cI) ? I * C + a : -1;
+    };
+
+    // Stage the Q rows in LDS: chunk c of row f at slot c ^ (f & 15).
+    for (int idx = threadIdx.x; idx < kScoreRows * CPR; idx += 256) {
+        const int f = idx / CPR, c = idx % CPR;
+        int I, h, i;
+        row_of(f, I, h, i);
+        uint4 v = zero_u4();
+        if (i >= 0) {
+            const int t = i * S + (h % S);
+            v = ld16(Q + ((size_t)t * Hq + h) * D + c * 8);
+        }
+        st16(&qs[f * D + ((c ^ (f & 15)) & (CPR - 1)) * 8], v);
+    }
+
+    // This lane's row in each tile.
+    int row_i[MT], row_h[MT];
+#pragma unroll
+    for (int rt = 0; rt < MT; ++rt) {
+        int I, h, i;
+        row_of(rt * 32 + q, I, h, i);
+        row_i[rt] = (rt < NT) ? i : -1;
+        row_h[rt] = h;
+    }
+    __syncthreads();
+
+    float rM[MT], rZ[MT];
+#pragma unroll
+    for (int rt = 0; rt < MT; ++rt) {
+        rM[rt] = -INFINITY;
+        rZ[rt] = 0.f;
+    }
+
+    // 32-stride units over the strides of blocks 0..Itop.
+    const int nu = ((Itop + 1) * C + 31) / 32;
+    const int nunits = (nu > wid) ? (nu - 1 - wid) / 4 + 1 : 0;
+    // Pooled-key row of this lane's A operand (see the permutation above).
+    const int krow = 16 * ((q >> 2) & 1) + 4 * (q >> 3) + (q & 3);
+    bf16x8 ka[3][NKS];
+    auto load_step = [&](int t, int ks) {
+        const int jr = min((wid + 4 * t) * 32 + krow, ns - 1);
+        const uint16_t *src = kb + (size_t)jr * D + ks * 16 + hk * 8;
+#pragma unroll
+        for (int p = 0; p < 3; ++p) ka[p][ks] = as_bf16x8(ld16(src + p * plane));
+    };
+    if (nunits > 0) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) load_step(0, ks);
+    }
+
+    // Q fragment ks of row tile rt (rows rt*32 + q: slot swizzle q & 15).
+    auto rdq = [&](int rt, int ks) {
+        const int c = 2 * ks + hk;
+        return as_bf16x8(ld16(&qs[(rt * 32 + q) * D + ((c ^ (q & 15)) & (CPR - 1)) * 8]));
+    };
+    bf16x8 qn[2] = {rdq(0, 0), rdq(0, 1)};
+
+    for (int t = 0; t < nunits; ++t) {
+        const int j0 = (wid + 4 * t) * 32;
+        const bool refill = t + 1 < nunits;
+        // Causal masking only where the unit reaches the first stride of block I0.
+        const bool diag = j0 + 31 >= I0 * C;
+#pragma unroll
+        for (int rt = 0; rt < MT; ++rt) {
+            if (rt >= NT) break;
+            const bool last = rt == NT - 1;
+            f32x16 acc;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+            // Q fragments are read from LDS two steps ahead of their products;
+            // the last two steps read the next tile's first two (tile 0 again
+            // after the last tile: the rows stay for every unit).
+            const int rt_next = last ? 0 : rt + 1;
+            bf16x8 qf[NKS];
+            qf[0] = qn[0];
+            qf[1] = qn[1];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                if (ks + 2 < NKS)
+                    qf[ks + 2] = rdq(rt, ks + 2);
+                else
+                    qn[ks + 2 - NKS] = rdq(rt_next, ks + 2 - NKS);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int p = 0; p < 3; ++p) acc = mfma32x32x16(ka[p][ks], qf[ks], acc);
+                if (last && refill) load_step(t + 1, ks);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const int ri = row_i[rt];
+            if (diag) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (j0 + 16 * hk + e > ri) acc[e] = -INFINITY;
+            }
+#pragma unroll
+            for (int bi = 0; bi < BPL; ++bi) {
+                float mr = -INFINITY;
+#pragma unroll
+                for (int e = bi * C; e < (bi + 1) * C; ++e) mr = fmaxf(mr, acc[e]);
+                const float m = mr * scale2;
+                const float mu = (mr == -INFINITY) ? 0.f : m;
+                // The block's C exponentials summed as two interleaved chains.
+                float z0 = fast_exp2(fmaf(acc[bi * C], scale2, -mu));
+                float z1 = fast_exp2(fmaf(acc[bi * C + 1], scale2, -mu));
+#pragma unroll
+                for (int e = 2; e < C; e += 2) {
+                    z0 += fast_exp2(fmaf(acc[bi * C + e], scale2, -mu));
+                    z1 += fast_exp2(fmaf(acc[bi * C + e + 1], scale2, -mu));
+                }
+                const float z = z0 + z1;
+                // A block with an unmasked stride j <= i lies at or before the
+                // row's own block.
+                const bool ok = ri >= 0 && mr != -INFINITY;
+                if (ok) {
+                    const int J = (j0 + 16 * hk) / C + bi;
+                    const int I = ri / C, a = ri - I * C;
+                    stats[(size_t)row_h[rt] * P + packed_offset(C, I, a, J)] = make_float2(m, z);
+                }
+                // Exact online merge into the row total with one exponential:
+                // e = 2^-|m - rM| scales whichever side is smaller.
+                {
+                    const float dd = m - rM[rt];
+                    const float e = fast_exp2(-fabsf(dd));
+                    const float nz = dd > 0.f ? fmaf(rZ[rt], e, z) : fmaf(z, e, rZ[rt]);
+                    rZ[rt] = ok ? nz : rZ[rt];
+                    rM[rt] = ok ? fmaxf(rM[rt], m) : rM[rt];
+                }
+            }
+        }
+    }
+
+    // Per-row totals: the two lane halves hold other blocks of the same row;
+    // then across waves.
+#pragma unroll
+    for (int rt = 0; rt < MT; ++rt) {
+        const float m2 = xor_lane(rM[rt], 32), z2 = xor_lane(rZ[rt], 32);
+        merge_max_sum(rM[rt], rZ[rt], m2, z2);
+    }
+    if (hk == 0) {
+#pragma unroll
+        for (int rt = 0; rt < MT; ++rt) red[wid][rt * 32 + q] = make_float2(rM[rt], rZ[rt]);
+    }
+    __syncthreads();
+    {
+        const int r = threadIdx.x;  // kScoreRows == 256 threads
+        float M = -INFINITY, Z = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) merge_max_sum(M, Z, red[w][r].x, red[w][r].y);
+        int I, h, i;
+        row_of(r, I, h, i);
+        if (i >= 0) rowstat[(size_t)h * ns + i] = make_float2(M, Z);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // rr_stride_softmax_pool: one work-group per (block-row I, query head h).
 // A[h][I][J] = sum_a z(a,J) 2^(m(a,J) - M_a) / Z_a over the strides a of
 // block I, i.e. the causal softmax of each sampled row summed over the
@@ -514,20 +726,21 @@ static void launch_score_d(const uint16_t *Q, const Shape &s, const EstimateWs &
     const int ngrp = (s.nb + R - 1) / R;
     const dim3 grid((unsigned)(ngrp * s.Hkv * nchunks));
     const float scale2 = kLog2e / sqrtf((float)D);
-#define RR_SCORE_CASE(CC)                                                                      \
+#define RR_SCORE_CASE(KERNEL, CC)                                                              \
     case CC:                                                                                   \
-        hipLaunchKernelGGL((rr_score<D, CC>), grid, dim3(256), 0, st, Q, w.kplanes, s.Hq, s.Hkv, \
+        hipLaunchKernelGGL((KERNEL<D, CC>), grid, dim3(256), 0, st, Q, w.kplanes, s.Hq, s.Hkv,    \
                            s.S, s.nb, s.ns, s.G, R, nchunks, s.P, scale2, w.stats, w.rowstat); \
         break;
+    // Blocks of 4 to 16 strides: 32 x 32 tiles, one lane per (row, block).
     switch (s.c) {
-        RR_SCORE_CASE(1)
-        RR_SCORE_CASE(2)
-        RR_SCORE_CASE(4)
-        RR_SCORE_CASE(8)
-        RR_SCORE_CASE(16)
-        RR_SCORE_CASE(32)
-        RR_SCORE_CASE(64)
-        RR_SCORE_CASE(128)
+        RR_SCORE_CASE(rr_score, 1)
+        RR_SCORE_CASE(rr_score, 2)
+        RR_SCORE_CASE(rr_score32, 4)
+        RR_SCORE_CASE(rr_score32, 8)
+        RR_SCORE_CASE(rr_score32, 16)
+        RR_SCORE_CASE(rr_score, 32)
+        RR_SCORE_CASE(rr_score, 64)
+        RR_SCORE_CASE(rr_score, 128)
         default: break;
     }
 #undef RR_SCORE_CASE

@@ -52,6 +52,9 @@ SMALL = [
     ("llama", 512, 4, 2, 128, 64, 32, 0.9),    # c = 2
     ("llama", 512, 4, 2, 128, 64, 64, 0.9),    # c = 1
     ("llama", 1024, 6, 3, 64, 128, 8, 0.5),
+    ("llama", 1024, 4, 2, 128, 64, 16, 0.9),   # c = 4, d = 128
+    ("llama", 768, 4, 2, 64, 128, 16, 0.9),    # c = 8, d = 64
+    ("llama", 1024, 32, 1, 64, 128, 8, 0.9),   # G = 32: 512 sampled rows per block-row, two row chunks
 ]
 
 
