@@ -156,7 +156,9 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
     const int I = nb - 1 - qi % nb;
 
     const int tid = threadIdx.x;
-    const int wid = tid >> 6, lane = tid & 63;
+    // The wave index is uniform: readfirstlane lets the compiler keep it and
+    // everything derived from it (LDS copy bases, head group) in SGPRs.
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int gr = wid / C::NWG;              // head group of this wave
     const int rw = wid % C::NWG;              // 32-row tile of this wave
     const int col = lane & 31, hk = lane >> 5;
