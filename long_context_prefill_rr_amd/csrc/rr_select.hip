@@ -9,7 +9,9 @@
 //
 // One work-group of 256 threads per row.  The row is sorted in LDS by a
 // bitonic network on 64-bit keys (float bits of the non-negative score in the
-// high word, ~J in the low word, so equal scores order by ascending J), the
+// high word, ~J in the low word, so equal scores order by ascending J; the
+// steps within one wave's quarter of the row run without work-group
+// barriers), the
 // sorted scores are prefix-summed with wave scans, the cut is found with an
 // LDS atomicMin, and kept flags are compacted in index order by a second scan.
 #include "rr_device.h"
@@ -77,22 +79,43 @@ __global__ __launch_bounds__(kSelThreads) void rr_topk_tau(const float *__restri
     if (tid == 0) cut = n - 1;
     __syncthreads();
 
-    // Bitonic sort, descending.
-    for (int k = 2; k <= N; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < N; i += kSelThreads) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const unsigned long long a = keys[i], b = keys[ixj];
-                    const bool desc = (i & k) == 0;
-                    if (desc ? (a < b) : (a > b)) {
-                        keys[i] = b;
-                        keys[ixj] = a;
-                    }
+    // Bitonic sort, descending.  Pair p of a step with partner distance j is
+    // (i, i + j) with i = (p / j) * 2j + p % j.  Each wave owns a segment of
+    // M = N/4 keys (the whole row in wave 0 when N < 256); steps with j < M
+    // stay inside one segment and run without work-group barriers (a wave's
+    // LDS accesses complete in order; the wait and the wave barrier keep the
+    // compiler from moving them across steps), so only the three steps with
+    // j >= M synchronise the work-group (none when N < 256).
+    {
+        const int wid = tid >> 6, lane = tid & 63;
+        const int M = N >= 256 ? N / 4 : N;
+        const int nseg = N / M;
+        auto cmpx = [&](int i, int j, int k) {
+            const unsigned long long a = keys[i], b = keys[i + j];
+            const bool desc = (i & k) == 0;
+            if (desc ? (a < b) : (a > b)) {
+                keys[i] = b;
+                keys[i + j] = a;
+            }
+        };
+        // j = 2^lj: the pair index splits with shifts and masks.
+        auto lower = [&](int p, int j, int lj) { return ((p >> lj) << (lj + 1)) | (p & (j - 1)); };
+        for (int k = 2; k <= N; k <<= 1) {
+            int lj = 31 - __clz(k >> 1);
+            for (int j = k >> 1; j > 0; j >>= 1, --lj) {
+                if (j >= M) {
+                    __syncthreads();
+                    for (int p = tid; p < N / 2; p += kSelThreads) cmpx(lower(p, j, lj), j, k);
+                    __syncthreads();
+                } else if (wid < nseg) {
+                    const int base = wid * M;
+                    for (int p = lane; p < M / 2; p += 64) cmpx(base + lower(p, j, lj), j, k);
+                    wait_lgkm0();
+                    __builtin_amdgcn_wave_barrier();
                 }
             }
-            __syncthreads();
         }
+        __syncthreads();
     }
 
     // Prefix sums of the sorted scores: thread t owns positions [t*E, t*E+E).
