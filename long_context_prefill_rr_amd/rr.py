@@ -1,9 +1,11 @@
 """ctypes binding of librr.so: the same calls as the C ABI (include/rr.h).
 
-Every function only checks tensor placement, dtype and contiguity, allocates
-outputs and workspace with torch when the caller does not pass them, and
-forwards device pointers plus the current HIP stream.  All arithmetic runs in
-the library's kernels.
+Every function only checks tensor shapes, placement, dtype and contiguity,
+allocates outputs and workspace with torch when the caller does not pass them,
+and forwards device pointers plus the current HIP stream.  All arithmetic runs
+in the library's kernels.  The shape checks matter: the C ABI takes bare
+pointers and sizes, so a tensor smaller than the sizes say would be read or
+written out of bounds on the device.
 
 Layouts: q [L][Hq][d], k and v [L][Hkv][d], all torch.bfloat16 on the GPU.
 """
@@ -94,6 +96,30 @@ def _dev(t, name, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _shape(t, name, shape):
+    """Refuse a tensor whose shape differs from the one the call reads or writes."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _nblocks(L, B):
+    if B <= 0 or L <= 0:
+        raise ValueError("L and B must be positive (L=%d, B=%d)" % (L, B))
+    return -(-L // B)
+
+
+def _qkv(q, k, v=None):
+    """(L, Hq, Hkv, d) from q [L][Hq][d]; k (and v) must be [L][Hkv][d]."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q and k must be 3-D ([L][heads][d])")
+    L, Hq, d = q.shape
+    Hkv = k.shape[1]
+    _shape(k, "k", (L, Hkv, d))
+    if v is not None:
+        _shape(v, "v", (L, Hkv, d))
+    return L, Hq, Hkv, d
+
+
 def _check(rc, where):
     if rc != 0:
         raise RRError(rc, where)
@@ -125,9 +151,9 @@ def _workspace(nbytes, device, ws):
 
 def rr_estimate(q, k, B, S, block_scores=None, ws=None, stream=None):
     """Block scores [Hq][nb][nb] (fp32) of the round-robin estimate."""
-    L, Hq, d = q.shape
-    Hkv = k.shape[1]
-    nb = -(-L // B)
+    L, Hq, Hkv, d = _qkv(q, k)
+    nb = _nblocks(L, B)
+    _shape(block_scores, "block_scores", (Hq, nb, nb))
     if block_scores is None:
         block_scores = torch.empty((Hq, nb, nb), dtype=torch.float32, device=q.device)
     lib = _load()
@@ -149,9 +175,9 @@ def rr_estimate_materialized(q, k, B, S, stride_scores=None, block_scores=None, 
     """(stride_scores, block_scores): every stride score written to memory
     (packed layout of include/rr.h, base-2 logits, -inf above the diagonal),
     then pooled; block_scores as for rr_estimate."""
-    L, Hq, d = q.shape
-    Hkv = k.shape[1]
-    nb = -(-L // B)
+    L, Hq, Hkv, d = _qkv(q, k)
+    nb = _nblocks(L, B)
+    _shape(block_scores, "block_scores", (Hq, nb, nb))
     lib = _load()
     n = lib.rr_stride_scores_count(L, Hq, Hkv, d, B, S)
     if stride_scores is None:
@@ -174,9 +200,9 @@ def rr_estimate_materialized(q, k, B, S, stride_scores=None, block_scores=None, 
 def rr_xattn_estimate(q, k, B, S, block_scores=None, ws=None, stream=None, average=False):
     """Block scores [Hq][nb][nb] (fp32) of XAttention's antidiagonal estimate
     (average=True: antidiagonal mean instead of sum)."""
-    L, Hq, d = q.shape
-    Hkv = k.shape[1]
-    nb = -(-L // B)
+    L, Hq, Hkv, d = _qkv(q, k)
+    nb = _nblocks(L, B)
+    _shape(block_scores, "block_scores", (Hq, nb, nb))
     if block_scores is None:
         block_scores = torch.empty((Hq, nb, nb), dtype=torch.float32, device=q.device)
     lib = _load()
@@ -191,7 +217,13 @@ def rr_xattn_estimate(q, k, B, S, block_scores=None, ws=None, stream=None, avera
 
 def rr_select(block_scores, L, B, tau, counts=None, block_idx=None, stream=None):
     """Top-tau selection: (counts [Hq][nb], block_idx [Hq][nb][nb]) int32."""
-    Hq, nb, _ = block_scores.shape
+    if block_scores.dim() != 3:
+        raise ValueError("block_scores must be 3-D ([Hq][nb][nb])")
+    Hq = block_scores.shape[0]
+    nb = _nblocks(L, B)
+    _shape(block_scores, "block_scores", (Hq, nb, nb))
+    _shape(counts, "counts", (Hq, nb))
+    _shape(block_idx, "block_idx", (Hq, nb, nb))
     dev = block_scores.device
     if counts is None:
         counts = torch.empty((Hq, nb), dtype=torch.int32, device=dev)
@@ -215,8 +247,11 @@ def _out_code(out_dtype):
 def rr_sparse_attn(q, k, v, B, counts, block_idx, out=None, out_dtype=torch.float32, ws=None,
                    stream=None):
     """Causal block-sparse GQA attention over the listed blocks -> O [L][Hq][d]."""
-    L, Hq, d = q.shape
-    Hkv = k.shape[1]
+    L, Hq, Hkv, d = _qkv(q, k, v)
+    nb = _nblocks(L, B)
+    _shape(counts, "counts", (Hq, nb))
+    _shape(block_idx, "block_idx", (Hq, nb, nb))
+    _shape(out, "out", (L, Hq, d))
     if out is None:
         out = torch.empty((L, Hq, d), dtype=out_dtype, device=q.device)
     code = _out_code(out.dtype)
@@ -234,9 +269,11 @@ def rr_sparse_attn(q, k, v, B, counts, block_idx, out=None, out_dtype=torch.floa
 def rr_prefill(q, k, v, B, S, tau, out=None, out_dtype=torch.bfloat16, counts=None,
                block_idx=None, ws=None, stream=None):
     """The whole sparse prefill: returns (O, counts, block_idx)."""
-    L, Hq, d = q.shape
-    Hkv = k.shape[1]
-    nb = -(-L // B)
+    L, Hq, Hkv, d = _qkv(q, k, v)
+    nb = _nblocks(L, B)
+    _shape(out, "out", (L, Hq, d))
+    _shape(counts, "counts", (Hq, nb))
+    _shape(block_idx, "block_idx", (Hq, nb, nb))
     dev = q.device
     if out is None:
         out = torch.empty((L, Hq, d), dtype=out_dtype, device=dev)
@@ -260,7 +297,17 @@ def rr_mask_quality(counts, block_idx, ref_counts, ref_block_idx, mass, L, B, ro
                     totals=None, stream=None):
     """Per-row (kept, ref, both, kept mass share) [Hq][nb][4] fp32 and their
     totals [5] fp64 (sums of the four columns, then the minimum share)."""
-    Hq, nb = counts.shape
+    if counts.dim() != 2:
+        raise ValueError("counts must be 2-D ([Hq][nb])")
+    Hq = counts.shape[0]
+    nb = _nblocks(L, B)
+    _shape(counts, "counts", (Hq, nb))
+    _shape(block_idx, "block_idx", (Hq, nb, nb))
+    _shape(ref_counts, "ref_counts", (Hq, nb))
+    _shape(ref_block_idx, "ref_block_idx", (Hq, nb, nb))
+    _shape(mass, "mass", (Hq, nb, nb))
+    _shape(rows, "rows", (Hq, nb, 4))
+    _shape(totals, "totals", (5,))
     dev = counts.device
     if rows is None:
         rows = torch.empty((Hq, nb, 4), dtype=torch.float32, device=dev)
@@ -292,9 +339,9 @@ def quality_summary(totals, n_rows):
 
 def rr_rescue_estimate(q, k, B, block_scores=None, ws=None, stream=None):
     """Rescue-branch block scores [Hq][nb][nb] (fp32, rows sum to 1)."""
-    L, Hq, d = q.shape
-    Hkv = k.shape[1]
-    nb = -(-L // B)
+    L, Hq, Hkv, d = _qkv(q, k)
+    nb = _nblocks(L, B)
+    _shape(block_scores, "block_scores", (Hq, nb, nb))
     if block_scores is None:
         block_scores = torch.empty((Hq, nb, nb), dtype=torch.float32, device=q.device)
     lib = _load()
@@ -309,7 +356,14 @@ def rr_rescue_estimate(q, k, B, block_scores=None, ws=None, stream=None):
 def rr_merge_masks(counts_a, block_idx_a, counts_b, block_idx_b, L, B, counts=None,
                    block_idx=None, stream=None):
     """Union of two block lists: (counts [Hq][nb], block_idx [Hq][nb][nb])."""
-    Hq, nb = counts_a.shape
+    if counts_a.dim() != 2:
+        raise ValueError("counts_a must be 2-D ([Hq][nb])")
+    Hq = counts_a.shape[0]
+    nb = _nblocks(L, B)
+    for t, name in ((counts_a, "counts_a"), (counts_b, "counts_b"), (counts, "counts")):
+        _shape(t, name, (Hq, nb))
+    for t, name in ((block_idx_a, "block_idx_a"), (block_idx_b, "block_idx_b"), (block_idx, "block_idx")):
+        _shape(t, name, (Hq, nb, nb))
     dev = counts_a.device
     if counts is None:
         counts = torch.empty((Hq, nb), dtype=torch.int32, device=dev)

@@ -117,6 +117,52 @@ def test_python_binding_rejects_cpu_tensors():
         rr.rr_estimate(q, q, 64, 8)
 
 
+def test_python_binding_rejects_wrong_shapes():
+    # The C ABI takes bare pointers and sizes; the binding refuses tensors
+    # whose shapes disagree with those sizes before anything reaches the
+    # library (CPU tensors of the right shapes then fail the placement check).
+    import torch
+    from long_context_prefill_rr_amd import rr
+    L, Hq, Hkv, d, B, S = 256, 4, 2, 64, 64, 8
+    nb = L // B
+    bf = dict(dtype=torch.bfloat16)
+    q, k, v = torch.zeros((L, Hq, d), **bf), torch.zeros((L, Hkv, d), **bf), torch.zeros((L, Hkv, d), **bf)
+    i32 = dict(dtype=torch.int32)
+    counts, idx = torch.zeros((Hq, nb), **i32), torch.zeros((Hq, nb, nb), **i32)
+    A = torch.zeros((Hq, nb, nb))
+    bad = [
+        lambda: rr.rr_estimate(q, torch.zeros((L - 8, Hkv, d), **bf), B, S),          # k shorter than q
+        lambda: rr.rr_estimate(q, k, B, S, block_scores=torch.zeros((Hq, nb, nb - 1))),
+        lambda: rr.rr_estimate(q, k, 0, S),                                             # B = 0
+        lambda: rr.rr_xattn_estimate(q, torch.zeros((L, Hkv, d + 8), **bf), B, S),
+        lambda: rr.rr_rescue_estimate(q, k, B, block_scores=torch.zeros((Hq + 1, nb, nb))),
+        lambda: rr.rr_estimate_materialized(q, k, B, S, block_scores=torch.zeros((Hq, nb, 1))),
+        lambda: rr.rr_select(A, L + B, B, 0.9),                                         # nb disagrees with L / B
+        lambda: rr.rr_select(A, L, B, 0.9, counts=torch.zeros((Hq, nb + 1), **i32)),
+        lambda: rr.rr_select(A, L, B, 0.9, block_idx=torch.zeros((Hq, nb, nb - 1), **i32)),
+        lambda: rr.rr_sparse_attn(q, k, torch.zeros((L, Hkv + 1, d), **bf), B, counts, idx),
+        lambda: rr.rr_sparse_attn(q, k, v, B, counts[:, :-1], idx),
+        lambda: rr.rr_sparse_attn(q, k, v, B, counts, idx, out=torch.zeros((L, Hq, d - 1))),
+        lambda: rr.rr_prefill(q, k, v, B, S, 0.9, out=torch.zeros((L - 1, Hq, d), **bf)),
+        lambda: rr.rr_prefill(q, k, v, B, S, 0.9, block_idx=idx[:, :, :-1]),
+        lambda: rr.rr_mask_quality(counts, idx, counts, idx, A[:, :, :-1], L, B),
+        lambda: rr.rr_mask_quality(counts, idx, counts, idx, A, L, B, totals=torch.zeros(4, dtype=torch.float64)),
+        lambda: rr.rr_merge_masks(counts, idx, counts, idx[:-1], L, B),
+    ]
+    for n, call in enumerate(bad):
+        with pytest.raises(ValueError):
+            call()
+    good = [
+        lambda: rr.rr_estimate(q, k, B, S, block_scores=A),
+        lambda: rr.rr_select(A, L, B, 0.9, counts=counts, block_idx=idx),
+        lambda: rr.rr_sparse_attn(q, k, v, B, counts, idx),
+        lambda: rr.rr_merge_masks(counts, idx, counts, idx, L, B),
+    ]
+    for call in good:
+        with pytest.raises(TypeError):   # right shapes, but host tensors
+            call()
+
+
 def test_mask_quality_validation(lib):
     args = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, 1024, 128, FAKE, FAKE, None]
     a = list(args); a[4] = None
