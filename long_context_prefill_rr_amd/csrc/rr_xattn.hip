@@ -15,19 +15,21 @@
 //
 // rr_xscore computes all x[h][i][j] as a GEMM with a fused statistics
 // epilogue: one work-group per (query head, tile of 256 query strides)
-// walks the key-stride tiles of 128 at or below its diagonal.  The
+// walks the key-stride tiles of 256 at or below its diagonal.  The
 // contraction runs in chunks of 64 elements (chunk kc covers t = kc/(d/64),
-// elements (kc mod d/64)*64 ..+63): the K~ tile [128 key strides][64] and
+// elements (kc mod d/64)*64 ..+63): the K~ tile [256 key strides][64] and
 // the Q~ tile [256 query strides][64] are copied global -> LDS with
-// global_load_lds_dwordx4 into a ring of three buffers, two chunks ahead of
-// the one being used.  Eight waves each own 64 key strides x 64 query
-// strides (2 x 2 tiles of v_mfma_f32_32x32x16_bf16, S^T orientation).  The key rows fed to the
+// buffer_load_dwordx4 ... lds into two buffers, one chunk ahead of the one
+// being used.  Eight waves each own 64 key strides x 128 query strides
+// (2 x 4 tiles of v_mfma_f32_32x32x16_bf16, S^T orientation): per 8
+// products a wave reads 6 fragments from LDS (1 per product with 2 x 2
+// tiles, which left the kernel bound by LDS bandwidth).  The key rows fed to the
 // matrix unit are permuted so that accumulator e of lane (query q, half hk)
 // holds key stride 16*hk + e of its 32-stride tile; after a key tile the
 // lane therefore has whole 16-stride runs of one query row and writes the
 // per-(row, block) max and sum of 2^(x - max) directly, in the packed layout
 // rr_stride_softmax_pool reads.  Row totals are merged across the lane
-// halves and the two key-half waves at the end.
+// halves and the four key-quarter waves at the end.
 #include "rr_device.h"
 #include "rr_internal.h"
 
@@ -36,12 +38,11 @@ namespace rr {
 namespace {
 
 constexpr int kXM = 256;        // query strides per work-group
-constexpr int kXT = 128;        // key strides per tile
+constexpr int kXT = 256;        // key strides per tile
 constexpr int kXK = 64;         // contraction elements per chunk
 constexpr int kXRowB = kXK * 2; // bytes per LDS row (8 slots of 16 bytes)
-constexpr int kXKB = kXT * kXRowB;   // bytes of one key tile chunk (16 KiB)
+constexpr int kXKB = kXT * kXRowB;   // bytes of one key tile chunk (32 KiB)
 constexpr int kXQB = kXM * kXRowB;   // bytes of one query tile chunk (32 KiB)
-constexpr int kXLPW = 6;        // copies per wave per chunk (2 key + 4 query)
 
 // Slot swizzles (16-byte slot XOR per row) for the two operands: the key
 // operand is read in the permuted row order, the query operand in natural
@@ -69,9 +70,7 @@ __global__ __launch_bounds__(512, 1) void rr_xscore(const uint16_t *__restrict__
     __shared__ __attribute__((aligned(1024))) char Qa0[kXQB];
     __shared__ __attribute__((aligned(1024))) char Ka1[kXKB];
     __shared__ __attribute__((aligned(1024))) char Qa1[kXQB];
-    __shared__ __attribute__((aligned(1024))) char Ka2[kXKB];
-    __shared__ __attribute__((aligned(1024))) char Qa2[kXQB];
-    __shared__ float2 red[2][kXM];
+    __shared__ float2 red[4][kXM];
 
     const int G = Hq / Hkv;
     const int bx = blockIdx.x;
@@ -84,14 +83,15 @@ __global__ __launch_bounds__(512, 1) void rr_xscore(const uint16_t *__restrict__
     const int total = ntn * nkc;
 
     const int tid = threadIdx.x;
-    const int wid = tid >> 6, lane = tid & 63;
+    // Uniform wave index: the copy destinations stay in scalar registers.
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 31, hk = lane >> 5;
-    const int wq = wid & 3, wk = wid >> 2;     // 64-query quarter, 64-key half
+    const int wq = wid & 1, wk = wid >> 1;     // 128-query half, 64-key quarter
 
     // Copies: lane l of an instruction writes slot l & 7 of row base + (l >> 3)
     // (8 rows x 128 bytes per instruction), holding element chunk
-    // (l & 7) ^ swz(row).  Wave w fills key rows 16w .. 16w+15 (2
-    // instructions) and query rows 32w .. 32w+31 (4 instructions).
+    // (l & 7) ^ swz(row).  Wave w fills key rows 32w .. 32w+31 and query rows
+    // 32w .. 32w+31 (4 instructions each).
     const int lrow = lane >> 3;
     const int cslot = lane & 7;
     // The copies are buffer loads: a resource based at the chunk's first key
@@ -106,12 +106,12 @@ __global__ __launch_bounds__(512, 1) void rr_xscore(const uint16_t *__restrict__
         const __amdgpu_buffer_rsrc_t rk = buf_rsrc(K + ((size_t)(jb * S + S - 1 - t) * Hkv + g) * D + e0);
         const __amdgpu_buffer_rsrc_t rq = buf_rsrc(Q + ((size_t)(ib * S + t) * Hq + h) * D + e0);
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const int r = 16 * wid + 8 * n + lrow;
+        for (int n = 0; n < 4; ++n) {
+            const int r = 32 * wid + 8 * n + lrow;
             const int j = min(j0 + r, ns - 1);  // >= jb
             const int ck = cslot ^ swz_key(r);
             const uint32_t off = (uint32_t)(((j - jb) * S * Hkv * D + ck * 8) * 2);
-            buf2lds16(rk, off, (lds_char *)ka + (16 * wid + 8 * n) * kXRowB);
+            buf2lds16(rk, off, (lds_char *)ka + (32 * wid + 8 * n) * kXRowB);
         }
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
@@ -126,19 +126,19 @@ __global__ __launch_bounds__(512, 1) void rr_xscore(const uint16_t *__restrict__
     // Key row fed to MFMA row `col`: accumulator e of lane (col, hk) is key
     // 16*hk + e of the 32-row tile.
     const int krow = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
-    int arow[2], brow[2];
+    constexpr int NA = 2, NB = 4;  // key and query 32-row tiles of a wave
+    int arow[NA], brow[NB];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        arow[u] = 64 * wk + 32 * u + krow;
-        brow[u] = 64 * wq + 32 * u + col;
-    }
+    for (int u = 0; u < NA; ++u) arow[u] = 64 * wk + 32 * u + krow;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) brow[u] = 128 * wq + 32 * u + col;
 
-    f32x16 acc[2][2];
+    f32x16 acc[NA][NB];
     auto zero_acc = [&]() {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < NA; ++a)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
     };
@@ -148,33 +148,38 @@ __global__ __launch_bounds__(512, 1) void rr_xscore(const uint16_t *__restrict__
 #pragma unroll
         for (int ks = 0; ks < kXK / 16; ++ks) {
             const int slot = ks * 2 + hk;
-            bf16x8 fa[2], fb[2];
+            bf16x8 fa[NA], fb[NB];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < NA; ++u)
                 fa[u] = *reinterpret_cast<const bf16x8 *>(ka + arow[u] * kXRowB + ((slot ^ swz_key(arow[u])) << 4));
+#pragma unroll
+            for (int u = 0; u < NB; ++u)
                 fb[u] = *reinterpret_cast<const bf16x8 *>(qa + brow[u] * kXRowB + ((slot ^ swz_query(brow[u])) << 4));
-            }
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int a = 0; a < NA; ++a)
 #pragma unroll
-                for (int b = 0; b < 2; ++b) acc[a][b] = mfma32x32x16(fa[a], fb[b], acc[a][b]);
+                for (int b = 0; b < NB; ++b) acc[a][b] = mfma32x32x16(fa[a], fb[b], acc[a][b]);
         }
     };
 
-    float rM[2] = {-INFINITY, -INFINITY}, rZ[2] = {0.f, 0.f};
-    int qi[2];
+    float rM[NB], rZ[NB];
+    int qi[NB];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) qi[b] = i0 + brow[b];
+    for (int b = 0; b < NB; ++b) {
+        rM[b] = -INFINITY;
+        rZ[b] = 0.f;
+        qi[b] = i0 + brow[b];
+    }
 
     // Statistics of one finished key tile.
     auto epilogue = [&](int tile) {
         const int j0 = tile * kXT;
         const bool masked = (j0 + kXT - 1 > i0);  // the tile reaches past the first query
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
+        for (int a = 0; a < NA; ++a) {
             const int jb = j0 + 64 * wk + 32 * a + 16 * hk;  // key stride of e = 0
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int b = 0; b < NB; ++b) {
                 const int i = qi[b];
                 float v[16];
 #pragma unroll
@@ -216,40 +221,30 @@ __global__ __launch_bounds__(512, 1) void rr_xscore(const uint16_t *__restrict__
         zero_acc();
     };
 
-    // Ring of three buffers, copies two chunks ahead.  A chunk's copies are
-    // waited for by their own wave (vmcnt, in issue order) and then by the
-    // barrier for everyone; the buffer refilled after the barrier was last
-    // read before it.  After an epilogue its stores also count in vmcnt, so
-    // the next wait drains everything.
-    bool stored = false;
+    // Two buffers, copies one chunk ahead.  Each wave waits for its own
+    // copies of the chunk (vmcnt, together with any statistics stores of the
+    // last epilogue), then the barrier for everyone's; the buffer refilled
+    // after the barrier was last read before it.
     auto step = [&](int idx, char *ka, char *qa, char *kn, char *qn) {
-        if (idx + 1 < total && !stored) wait_vmcnt<kXLPW>();
-        else wait_vmcnt<0>();
-        stored = false;
+        wait_vmcnt<0>();
         bar();
         // Past the end the last chunk is copied again, into a buffer no one
         // reads any more: every step issues the same copies.
-        issue(min(idx + 2, total - 1), kn, qn);
+        issue(min(idx + 1, total - 1), kn, qn);
         compute(ka, qa);
-        if ((idx + 1) % nkc == 0) {
-            epilogue(idx / nkc);
-            stored = true;
-        }
+        if ((idx + 1) % nkc == 0) epilogue(idx / nkc);
     };
     issue(0, Ka0, Qa0);
-    issue(min(1, total - 1), Ka1, Qa1);
-    for (int idx = 0; idx < total; idx += 3) {
-        step(idx, Ka0, Qa0, Ka2, Qa2);
+    for (int idx = 0; idx < total; idx += 2) {
+        step(idx, Ka0, Qa0, Ka1, Qa1);
         if (idx + 1 >= total) break;
         step(idx + 1, Ka1, Qa1, Ka0, Qa0);
-        if (idx + 2 >= total) break;
-        step(idx + 2, Ka2, Qa2, Ka1, Qa1);
     }
     wait_vmcnt<0>();
 
-    // Row totals: the two lane halves, then the two key-half waves.
+    // Row totals: the two lane halves, then the four key-quarter waves.
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < NB; ++b) {
         float m2 = xor_lane(rM[b], 32), z2 = xor_lane(rZ[b], 32);
         if (C == 32) {  // both halves hold the same blocks: hk = 1 wrote nothing
             m2 = -INFINITY;
@@ -260,13 +255,13 @@ __global__ __launch_bounds__(512, 1) void rr_xscore(const uint16_t *__restrict__
     __syncthreads();
     if (hk == 0) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) red[wk][brow[b]] = make_float2(rM[b], rZ[b]);
+        for (int b = 0; b < NB; ++b) red[wk][brow[b]] = make_float2(rM[b], rZ[b]);
     }
     __syncthreads();
     if (tid < kXM) {
         float M = -INFINITY, Z = 0.f;
-        merge_max_sum(M, Z, red[0][tid].x, red[0][tid].y);
-        merge_max_sum(M, Z, red[1][tid].x, red[1][tid].y);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) merge_max_sum(M, Z, red[w][tid].x, red[w][tid].y);
         const int i = i0 + tid;
         if (i < ns) rowstat[(size_t)h * ns + i] = make_float2(M, Z);
     }
