@@ -334,16 +334,17 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
         }
 
         // V^T fragments of 16-key group gi (kt = gi / 2, mm = gi % 2), one per
-        // 32-row d-tile; group 0's are read before the softmax starts and
-        // each later group's while the previous group's products run.
+        // 32-row d-tile; groups 0 and 1 are read before the softmax starts and
+        // each later group's two groups ahead of its products.
         auto rdv = [&](int gi, uint4 (&a)[C::NDT]) {
             const int voff = ((4 * (gi >> 1) + 2 * hk + (gi & 1)) ^ vsw) << 4;
 #pragma unroll
             for (int dt = 0; dt < C::NDT; ++dt)
                 a[dt] = *reinterpret_cast<const uint4 *>(vb + (dt * 32 + col) * (C::KT * 2) + voff);
         };
-        uint4 va[C::NDT], vn[C::NDT];
-        rdv(0, va);
+        uint4 vf[4][C::NDT];
+        rdv(0, vf[0]);
+        rdv(1, vf[1]);
         __builtin_amdgcn_sched_barrier(0);
 
         if (diag) {
@@ -391,12 +392,10 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
             }
             lsum += gsum;
             const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-            if (gi + 1 < 4) rdv(gi + 1, vn);
+            if (gi + 2 < 4) rdv(gi + 2, vf[gi + 2]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) o[dt] = mfma32x32x16(as_bf16x8(va[dt]), pb, o[dt]);
-#pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) va[dt] = vn[dt];
+            for (int dt = 0; dt < C::NDT; ++dt) o[dt] = mfma32x32x16(as_bf16x8(vf[gi][dt]), pb, o[dt]);
         }
     };
 
