@@ -485,6 +485,8 @@ def main():
         "dense_attention_ms": dense_ms,
         "speedup_vs_dense_attention": None if dense_ms is None else dense_ms / ms,
         "density": n_kept / causal_blocks,
+        "density_per_head": [round(float(x), 4) for x in
+                             (counts.clamp(min=0).sum(dim=1).double() / (nb * (nb + 1) // 2)).cpu().tolist()],
         "selection_quality": quality,
         "xattn_comparison": xattn,
         "rescue_branch": rescue,
