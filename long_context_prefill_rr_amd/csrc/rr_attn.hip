@@ -20,10 +20,12 @@
 //   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16.  The K rows fed to the
 //     matrix unit are permuted so that accumulator register e of lane
 //     (column q, half hk) holds key 16*hk + e of each 32-key sub-tile:
-//     every lane owns one query column, and the row softmax needs a single
-//     cross-half exchange;
+//     every lane owns one query column, and a row maximum, when one is
+//     taken, needs a single cross-half exchange;
 //   * online softmax in the log2 domain (scores pre-scaled by
-//     log2(e)/sqrt(d)), diagonal block masked causally;
+//     log2(e)/sqrt(d)), diagonal block masked causally; the running maximum
+//     is checked through each 16-key group's weight sum rather than taken
+//     per score;
 //   * P^T is rounded to bf16 in registers and used directly as the B operand
 //     of O^T += V^T . P^T: its registers already hold 8 consecutive keys per
 //     lane half, and the matching V^T rows are 16-byte LDS reads.
