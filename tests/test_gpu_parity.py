@@ -55,6 +55,8 @@ SMALL = [
     ("llama", 1024, 4, 2, 128, 64, 16, 0.9),   # c = 4, d = 128
     ("llama", 768, 4, 2, 64, 128, 16, 0.9),    # c = 8, d = 64
     ("llama", 1024, 32, 1, 64, 128, 8, 0.9),   # G = 32: 512 sampled rows per block-row, two row chunks
+    ("llama", 4096, 4, 2, 64, 64, 8, 0.9),     # 64-row blocks, 64 block-rows: long lists in the B = 64 kernel
+    ("llama", 2048, 16, 2, 128, 64, 4, 0.9),   # B = 64 at d = 128, G = 8 (four head pairs), c = 16
 ]
 
 
