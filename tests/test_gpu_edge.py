@@ -7,7 +7,10 @@ the largest supported block count.
 * tau so small that exactly one block (the largest, earliest on ties) is
   kept per row;
 * rr_select on rows of equal scores, all-zero rows included;
-* nb = 4096 (L = 524288 at B = 128), the largest list the selection sorts:
+* rr_select on long rows (nb up to 4096) of dyadic scores drawn from a few
+  levels, so most cuts fall inside a run of ties: every sum is exact in
+  fp32 and fp64 alike, so the lists must equal the oracle's exactly;
+* nb = 4096 (L = 524288 at B = 128), the largest list the selection takes:
   end to end, checked on sampled block-rows and tokens.
 Rules as for the other parity tests: masks equal up to blocks within 1e-4 of
 the tau boundary, block scores to 1e-5 of the row total, attention outputs
@@ -94,6 +97,32 @@ def test_select_equal_and_zero_rows():
         assert list_is_well_formed(counts, idx)
         assert np.array_equal(mask_from_list(counts, idx, nb), keep_o.astype(np.uint8))
         assert np.array_equal(counts, cnt_o)
+
+
+@pytest.mark.parametrize("nb", [64, 1000, 4096])
+def test_select_exact_on_dyadic_rows_with_ties(nb):
+    """Scores are multiples of 2^-6 no larger than 1 and tau is a multiple of
+    2^-4, so row totals, running sums and tau * total are exact in fp32 (at
+    most 22 significant bits) and the selection has one right answer."""
+    rr = _rr()
+    rng = np.random.default_rng(100 + nb)
+    levels = np.array([0.0, 1 / 64, 1 / 16, 0.25, 0.5, 1.0], dtype=np.float32)
+    Hq = 2
+    A = rng.choice(levels, size=(Hq, nb, nb)).astype(np.float32)
+    A *= np.tril(np.ones((nb, nb), dtype=np.float32))[None]
+    A[1, nb // 3] = 0.0                     # an all-zero row: the first block is kept
+    A[0, nb - 1, : nb // 2] = 0.25          # a long run of equal scores at the start of the last row
+    A_dev = torch.from_numpy(A).cuda()
+    print("select dyadic nb=%d" % nb, flush=True)
+    for tau in (0.5, 0.75, 0.875, 0.9375):
+        counts, idx = rr.rr_select(A_dev, nb * 64, 64, tau)
+        torch.cuda.synchronize()
+        counts, idx = counts.cpu().numpy(), idx.cpu().numpy()
+        keep_o, cnt_o, _ = oracle.select(A.astype(np.float64), tau)
+        assert list_is_well_formed(counts, idx)
+        assert np.array_equal(counts, cnt_o), tau
+        assert np.array_equal(mask_from_list(counts, idx, nb), keep_o.astype(np.uint8)), tau
+        assert counts[1, nb // 3] == 1 and idx[1, nb // 3, 0] == 0
 
 
 def test_largest_block_count():
