@@ -12,7 +12,7 @@ using namespace rr;
 
 namespace {
 
-constexpr int kMaxBlocks = 4096;  // longest Top-tau row the selection kernel sorts
+constexpr int kMaxBlocks = 4096;  // longest Top-tau row the selection kernel holds (64 per lane)
 constexpr int kMaxHeads = 1024;   // query heads per call
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
