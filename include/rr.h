@@ -62,8 +62,19 @@ const char *rr_status_str(int status);
 int rr_abi_version(void);
 
 /*
- * Workspace sizes in bytes (0 if the shape is invalid).  The prefill size is
- * large enough for each of the three stage calls as well.
+ * rr_workspace_bytes -- one workspace size for a shape: the largest amount of
+ * device workspace any entry point of this header needs for (L, Hq, Hkv, d,
+ * B, S) (rr_estimate, rr_sparse_attn, rr_prefill, rr_xattn_estimate,
+ * rr_estimate_materialized and rr_rescue_estimate), so that one caller-owned
+ * buffer of this size serves every call on that shape.  0 if the shape is
+ * invalid or unsupported (the same checks as the calls themselves).
+ */
+size_t rr_workspace_bytes(int L, int Hq, int Hkv, int d, int B, int S);
+
+/*
+ * Per-call workspace sizes in bytes (0 if the shape is invalid), each <=
+ * rr_workspace_bytes.  The prefill size is large enough for each of the
+ * three stage calls as well.
  */
 size_t rr_estimate_workspace_bytes(int L, int Hq, int Hkv, int d, int B, int S);
 size_t rr_sparse_attn_workspace_bytes(int L, int Hq, int Hkv, int d, int B);
@@ -121,7 +132,11 @@ int rr_estimate_materialized(const uint16_t *Q, const uint16_t *K, int L, int Hq
  * whose cumulative score is >= tau * W (find_blocks, XAttention review page,
  * threshold block selection); tau = 1 keeps every causal block.  Sums run in
  * fp32.
- *   block_scores  in, fp32 [Hq][nb][nb] (as written by rr_estimate).
+ *   block_scores  in, fp32 [Hq][nb][nb] (as written by rr_estimate).  The
+ *                 rule is defined for finite scores >= 0, which is what the
+ *                 estimators write; an entry J <= I that is negative, NaN or
+ *                 infinite is read as 0 (zero mass, ordered by J among the
+ *                 other zeros), so such input cannot break the ordering.
  *   counts        out, int32 [Hq][nb]: number of kept blocks (>= 1).
  *   block_idx     out, int32 [Hq][nb][nb]: kept key-block indices of row
  *                 (h, I) in ascending order in its first counts[h][I]

@@ -65,6 +65,35 @@ int run_attn(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const Shap
 
 }  // namespace
 
+namespace rr {
+
+int check_prefill_args(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, int Hq,
+                       int Hkv, int d, int B, int S, float tau, const void *O, int o_dtype,
+                       const int32_t *counts, const int32_t *block_idx) {
+    if (!Q || !K || !V || !O || !counts || !block_idx) return RR_E_NULL;
+    int rc = check_shape(L, Hq, Hkv, d, B, S, true);
+    if (rc != RR_OK) return rc;
+    rc = check_tau(tau);
+    if (rc != RR_OK) return rc;
+    if (o_dtype != RR_OUT_BF16 && o_dtype != RR_OUT_F32) return RR_E_UNSUPPORTED;
+    return RR_OK;
+}
+
+int run_prefill(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, int Hq, int Hkv,
+                int d, int B, int S, float tau, void *O, int o_dtype, int32_t *counts,
+                int32_t *block_idx, void *ws, void *stream) {
+    const Shape s = make_shape(L, Hq, Hkv, d, B, S);
+    hipStream_t st = as_stream(stream);
+    float *A = (float *)ws;
+    void *rest = (char *)ws + align_up((size_t)s.Hq * s.nb * s.nb * 4);
+    int rc = run_estimate(Q, K, s, A, rest, st);
+    if (rc != RR_OK) return rc;
+    if (launch_topk_tau(A, s, tau, counts, block_idx, st) != hipSuccess) return RR_E_HIP;
+    return run_attn(Q, K, V, s, counts, block_idx, O, o_dtype, rest, st);
+}
+
+}  // namespace rr
+
 extern "C" {
 
 const char *rr_status_str(int status) {
@@ -98,6 +127,16 @@ size_t rr_prefill_workspace_bytes(int L, int Hq, int Hkv, int d, int B, int S) {
     const size_t a = align_up((size_t)s.Hq * s.nb * s.nb * 4);
     const size_t e = estimate_ws_bytes(s), t = attn_ws_bytes(s);
     return a + (e > t ? e : t);
+}
+
+size_t rr_workspace_bytes(int L, int Hq, int Hkv, int d, int B, int S) {
+    if (check_shape(L, Hq, Hkv, d, B, S, true) != RR_OK) return 0;
+    // The prefill size covers rr_estimate, rr_xattn_estimate (same layout),
+    // the materialised estimate (its pooled-key planes only) and
+    // rr_sparse_attn; the rescue branch has its own layout.
+    const size_t p = rr_prefill_workspace_bytes(L, Hq, Hkv, d, B, S);
+    const size_t r = rescue_ws_bytes(make_shape(L, Hq, Hkv, d, B, S));
+    return p > r ? p : r;
 }
 
 int rr_estimate(const uint16_t *Q, const uint16_t *K, int L, int Hq, int Hkv, int d, int B, int S,
@@ -171,21 +210,13 @@ int rr_sparse_attn(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int 
 int rr_prefill(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, int Hq, int Hkv,
                int d, int B, int S, float tau, void *O, int o_dtype, int32_t *counts,
                int32_t *block_idx, void *ws, size_t ws_bytes, void *stream) {
-    if (!Q || !K || !V || !O || !counts || !block_idx || !ws) return RR_E_NULL;
-    int rc = check_shape(L, Hq, Hkv, d, B, S, true);
+    if (!ws) return RR_E_NULL;
+    const int rc = rr::check_prefill_args(Q, K, V, L, Hq, Hkv, d, B, S, tau, O, o_dtype, counts,
+                                          block_idx);
     if (rc != RR_OK) return rc;
-    rc = check_tau(tau);
-    if (rc != RR_OK) return rc;
-    if (o_dtype != RR_OUT_BF16 && o_dtype != RR_OUT_F32) return RR_E_UNSUPPORTED;
-    const Shape s = make_shape(L, Hq, Hkv, d, B, S);
     if (ws_bytes < rr_prefill_workspace_bytes(L, Hq, Hkv, d, B, S)) return RR_E_WORKSPACE;
-    hipStream_t st = as_stream(stream);
-    float *A = (float *)ws;
-    void *rest = (char *)ws + align_up((size_t)s.Hq * s.nb * s.nb * 4);
-    rc = run_estimate(Q, K, s, A, rest, st);
-    if (rc != RR_OK) return rc;
-    if (launch_topk_tau(A, s, tau, counts, block_idx, st) != hipSuccess) return RR_E_HIP;
-    return run_attn(Q, K, V, s, counts, block_idx, O, o_dtype, rest, st);
+    return rr::run_prefill(Q, K, V, L, Hq, Hkv, d, B, S, tau, O, o_dtype, counts, block_idx, ws,
+                           stream);
 }
 
 int rr_mask_quality(const int32_t *counts, const int32_t *block_idx, const int32_t *ref_counts,

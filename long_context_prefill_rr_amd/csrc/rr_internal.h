@@ -66,6 +66,16 @@ inline long long score_elems_per_head(const Shape &s) { return (long long)s.c * 
 // Attention workspace: V transposed to [Hkv][d][nb*B] (zero-padded tail).
 inline size_t attn_ws_bytes(const Shape &s) { return align_up((size_t)s.Hkv * s.d * s.nb * s.B * 2); }
 
+// rr_prefill's host-side argument checks (everything but the workspace) and
+// its launch sequence on a workspace of at least rr_prefill_workspace_bytes;
+// both return an rr_status code.
+int check_prefill_args(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, int Hq,
+                       int Hkv, int d, int B, int S, float tau, const void *O, int o_dtype,
+                       const int32_t *counts, const int32_t *block_idx);
+int run_prefill(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, int Hq, int Hkv,
+                int d, int B, int S, float tau, void *O, int o_dtype, int32_t *counts,
+                int32_t *block_idx, void *ws, void *stream);
+
 // Launchers (enqueue on `stream`, return the launch error).
 hipError_t launch_pool_k(const uint16_t *K, const Shape &s, uint16_t *kplanes, hipStream_t st);
 hipError_t launch_score(const uint16_t *Q, const Shape &s, const EstimateWs &w, hipStream_t st);

@@ -57,6 +57,10 @@ __device__ __forceinline__ int wave_min_i(int v) {
 // integers; slots past the row hold -0.0, whose bits read as INT_MIN, below
 // every non-negative score, so no threshold selects them, no tie matches
 // them, and a sum they do enter gains nothing.
+//
+// The rule is defined for finite scores >= 0.  An entry that is negative,
+// NaN or infinite is read as +0.0 (zero mass), so the bit order and the
+// monotone mass search hold for any input.
 template <int NE>
 __device__ __forceinline__ void topk_row(const float *__restrict__ row, int n, int nb, float tau,
                                          int32_t *__restrict__ out, int32_t *__restrict__ count) {
@@ -65,7 +69,12 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ row, int n, i
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
         const int J = 64 * e + lane;
-        x[e] = J < n ? row[J] : -0.f;
+        if (J < n) {
+            const float v = row[J];
+            x[e] = (v > 0.f && v <= 3.402823466e38f) ? v : 0.f;
+        } else {
+            x[e] = -0.f;
+        }
     }
 
     int kept = n;

@@ -52,6 +52,8 @@ def _load():
         lib.rr_status_str.argtypes = [i]
         lib.rr_status_str.restype = ctypes.c_char_p
         lib.rr_abi_version.restype = i
+        lib.rr_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        lib.rr_workspace_bytes.restype = z
         lib.rr_estimate_workspace_bytes.argtypes = [i, i, i, i, i, i]
         lib.rr_estimate_workspace_bytes.restype = z
         lib.rr_sparse_attn_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -123,6 +125,11 @@ def _qkv(q, k, v=None):
 def _check(rc, where):
     if rc != 0:
         raise RRError(rc, where)
+
+
+def workspace_bytes(L, Hq, Hkv, d, B, S):
+    """Bytes of one workspace that serves every call on this shape (0: invalid)."""
+    return _load().rr_workspace_bytes(L, Hq, Hkv, d, B, S)
 
 
 def estimate_workspace_bytes(L, Hq, Hkv, d, B, S):

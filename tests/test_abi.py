@@ -86,6 +86,26 @@ def test_workspace_sizes(lib):
     assert a >= 3 * 8 * ns * 128 * 2 + 32 * P * 8 + 32 * ns * 8
 
 
+def test_one_workspace_size_serves_every_call(lib):
+    # rr_workspace_bytes(L, Hq, Hkv, d, B, S): the largest workspace any call
+    # needs on the shape, so one buffer of that size serves them all.
+    for L, Hq, Hkv, d, B, S in [(8192, 32, 8, 128, 128, 8), (1216, 7, 1, 64, 64, 16),
+                                (131072, 32, 8, 128, 128, 8), (1024, 8, 8, 64, 128, 1),
+                                (65536, 28, 4, 128, 128, 16)]:
+        w = lib.rr_workspace_bytes(L, Hq, Hkv, d, B, S)
+        per_call = [lib.rr_estimate_workspace_bytes(L, Hq, Hkv, d, B, S),
+                    lib.rr_sparse_attn_workspace_bytes(L, Hq, Hkv, d, B),
+                    lib.rr_prefill_workspace_bytes(L, Hq, Hkv, d, B, S),
+                    lib.rr_rescue_workspace_bytes(L, Hq, Hkv, d, B),
+                    lib.rr_estimate_materialized_workspace_bytes(L, Hq, Hkv, d, B, S)]
+        assert w > 0 and w == max(per_call), (L, Hq, Hkv, d, B, S, w, per_call)
+    # Invalid or unsupported shapes give 0, as the calls reject them.
+    assert lib.rr_workspace_bytes(1004, 8, 2, 128, 128, 8) == 0      # L % S
+    assert lib.rr_workspace_bytes(1024, 6, 4, 128, 128, 8) == 0      # Hq % Hkv
+    assert lib.rr_workspace_bytes(1024, 8, 2, 96, 128, 8) == 0       # d
+    assert lib.rr_workspace_bytes(1024, 8, 2, 128, 128, 12) == 0     # B % S
+
+
 def test_select_and_attn_validation(lib):
     f = ctypes.c_float
     assert lib.rr_select(FAKE, 8, 1024, 128, f(0.0), FAKE, FAKE, None) == RR_E_TAU

@@ -6,7 +6,8 @@ the largest supported block count.
   only Hq of the S positions), one head, eight query heads per kv-head;
 * tau so small that exactly one block (the largest, earliest on ties) is
   kept per row;
-* rr_select on rows of equal scores, all-zero rows included;
+* rr_select on rows of equal scores, all-zero rows included, and on rows
+  holding negative, NaN or infinite entries (read as 0, as documented);
 * rr_select on long rows (nb up to 4096) of dyadic scores drawn from a few
   levels, so most cuts fall inside a run of ties: every sum is exact in
   fp32 and fp64 alike, so the lists must equal the oracle's exactly;
@@ -123,6 +124,38 @@ def test_select_exact_on_dyadic_rows_with_ties(nb):
         assert np.array_equal(counts, cnt_o), tau
         assert np.array_equal(mask_from_list(counts, idx, nb), keep_o.astype(np.uint8)), tau
         assert counts[1, nb // 3] == 1 and idx[1, nb // 3, 0] == 0
+
+
+def test_select_reads_invalid_scores_as_zero():
+    """rr_select's rule is defined for finite scores >= 0; a negative, NaN or
+    infinite entry is documented to count as 0.  The result must equal the
+    oracle's selection on the row with those entries set to 0 (dyadic values,
+    so every sum is exact and the answer unique)."""
+    rr = _rr()
+    rng = np.random.default_rng(7)
+    nb, Hq = 96, 2
+    levels = np.array([0.0, 1 / 64, 1 / 16, 0.25, 0.5, 1.0], dtype=np.float32)
+    clean = rng.choice(levels, size=(Hq, nb, nb)).astype(np.float32)
+    clean *= np.tril(np.ones((nb, nb), dtype=np.float32))[None]
+    dirty = clean.copy()
+    bad = np.array([-1.0, -0.0, np.nan, np.inf, -np.inf, -3e38], dtype=np.float32)
+    for h in range(Hq):
+        for I in range(nb):
+            for J in rng.choice(I + 1, size=min(I + 1, 3), replace=False):
+                dirty[h, I, J] = bad[rng.integers(len(bad))]
+                clean[h, I, J] = 0.0
+    dirty[1, 5, :6] = np.nan                    # a row with no valid entry: block 0 is kept
+    clean[1, 5, :6] = 0.0
+    for tau in (0.5, 0.875, 1.0):
+        counts, idx = rr.rr_select(torch.from_numpy(dirty).cuda(), nb * 64, 64, tau)
+        torch.cuda.synchronize()
+        counts, idx = counts.cpu().numpy(), idx.cpu().numpy()
+        keep_o, cnt_o, _ = oracle.select(clean.astype(np.float64), tau)
+        assert list_is_well_formed(counts, idx)
+        assert np.array_equal(counts, cnt_o), tau
+        assert np.array_equal(mask_from_list(counts, idx, nb), keep_o.astype(np.uint8)), tau
+        if tau < 1.0:
+            assert counts[1, 5] == 1 and idx[1, 5, 0] == 0
 
 
 def test_largest_block_count():
