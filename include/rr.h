@@ -170,6 +170,28 @@ int rr_prefill(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, i
                int32_t *block_idx, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * rr_prefill_noalloc -- rr_prefill for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same checks, kernels and results as rr_prefill, with
+ * the workspace taken from a device array the library owns instead of from
+ * the caller.  It allocates nothing and frees nothing.
+ *   Arguments as for rr_prefill, minus ws / ws_bytes.
+ *   Size limit: shapes whose rr_prefill_workspace_bytes(...) exceeds
+ *   rr_noalloc_scratch_bytes() (64 MiB; e.g. L = 16384 at 32/8 heads, d = 128,
+ *   B = 128, S = 8 fits, L = 32768 does not) return RR_E_WORKSPACE.
+ *   `stream` must belong to the current device (else RR_E_UNSUPPORTED).
+ * Every GPU the library runs on holds one 64 MiB array until the process
+ * ends; its device address is looked up on the first call made on that
+ * device.  All calls on one GPU share that array: calls that overlap on one
+ * GPU (on different streams, or from several host threads) race and give
+ * undefined results; calls ordered on one stream are safe.
+ */
+size_t rr_noalloc_scratch_bytes(void);
+int rr_prefill_noalloc(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, int Hq,
+                       int Hkv, int d, int B, int S, float tau, void *O, int o_dtype,
+                       int32_t *counts, int32_t *block_idx, void *stream);
+
+/*
  * rr_xattn_estimate -- XAttention's antidiagonal block scores (XAttention
  * review page, "importance prediction" and "threshold block selection"
  * steps 1-2), the estimator the RRAttention pages compare against, on the

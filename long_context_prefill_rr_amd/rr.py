@@ -64,6 +64,9 @@ def _load():
         lib.rr_select.argtypes = [P, i, i, i, f, P, P, P]
         lib.rr_sparse_attn.argtypes = [P, P, P, i, i, i, i, i, P, P, P, i, P, z, P]
         lib.rr_prefill.argtypes = [P, P, P, i, i, i, i, i, i, f, P, i, P, P, P, z, P]
+        lib.rr_noalloc_scratch_bytes.argtypes = []
+        lib.rr_noalloc_scratch_bytes.restype = z
+        lib.rr_prefill_noalloc.argtypes = [P, P, P, i, i, i, i, i, i, f, P, i, P, P, P]
         lib.rr_mask_quality.argtypes = [P, P, P, P, P, i, i, i, P, P, P]
         lib.rr_xattn_estimate.argtypes = [P, P, i, i, i, i, i, i, i, P, P, z, P]
         lib.rr_rescue_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -75,7 +78,8 @@ def _load():
         lib.rr_estimate_materialized_workspace_bytes.argtypes = [i, i, i, i, i, i]
         lib.rr_estimate_materialized_workspace_bytes.restype = z
         lib.rr_estimate_materialized.argtypes = [P, P, i, i, i, i, i, i, P, P, P, z, P]
-        for name in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill", "rr_mask_quality",
+        for name in ("rr_estimate", "rr_select", "rr_sparse_attn", "rr_prefill", "rr_prefill_noalloc",
+                     "rr_mask_quality",
                      "rr_xattn_estimate", "rr_rescue_estimate", "rr_merge_masks",
                      "rr_estimate_materialized"):
             getattr(lib, name).restype = i
@@ -297,6 +301,37 @@ def rr_prefill(q, k, v, B, S, tau, out=None, out_dtype=torch.bfloat16, counts=No
                         _dev(block_idx, "block_idx", torch.int32), _dev(ws, "ws"),
                         ws.numel() * ws.element_size(), _stream_ptr(stream))
     _check(rc, "rr_prefill")
+    return out, counts, block_idx
+
+
+def noalloc_scratch_bytes():
+    """Bytes of the library-owned workspace rr_prefill_noalloc uses on each GPU."""
+    return _load().rr_noalloc_scratch_bytes()
+
+
+def rr_prefill_noalloc(q, k, v, B, S, tau, out=None, out_dtype=torch.bfloat16, counts=None,
+                       block_idx=None, stream=None):
+    """rr_prefill with the library's own workspace (no workspace argument, no
+    device allocation inside the call): returns (O, counts, block_idx).  Pass
+    out, counts and block_idx to keep this wrapper from allocating them."""
+    L, Hq, Hkv, d = _qkv(q, k, v)
+    nb = _nblocks(L, B)
+    _shape(out, "out", (L, Hq, d))
+    _shape(counts, "counts", (Hq, nb))
+    _shape(block_idx, "block_idx", (Hq, nb, nb))
+    dev = q.device
+    if out is None:
+        out = torch.empty((L, Hq, d), dtype=out_dtype, device=dev)
+    if counts is None:
+        counts = torch.empty((Hq, nb), dtype=torch.int32, device=dev)
+    if block_idx is None:
+        block_idx = torch.empty((Hq, nb, nb), dtype=torch.int32, device=dev)
+    code = _out_code(out.dtype)
+    rc = _load().rr_prefill_noalloc(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
+                                    _dev(v, "v", torch.bfloat16), L, Hq, Hkv, d, B, S, float(tau),
+                                    _dev(out, "out"), code, _dev(counts, "counts", torch.int32),
+                                    _dev(block_idx, "block_idx", torch.int32), _stream_ptr(stream))
+    _check(rc, "rr_prefill_noalloc")
     return out, counts, block_idx
 
 

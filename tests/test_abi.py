@@ -106,6 +106,25 @@ def test_one_workspace_size_serves_every_call(lib):
     assert lib.rr_workspace_bytes(1024, 8, 2, 128, 128, 12) == 0     # B % S
 
 
+def test_noalloc_prefill_validation(lib):
+    # Host-side checks run before any HIP call: the rr_prefill rules, then the
+    # size of the library-owned workspace.
+    assert lib.rr_noalloc_scratch_bytes() == 64 << 20
+    f = ctypes.c_float
+    def p(L=1024, Hq=8, Hkv=2, d=128, B=128, S=8, tau=0.9, Q=FAKE, o_dtype=0):
+        return lib.rr_prefill_noalloc(Q, FAKE, FAKE, L, Hq, Hkv, d, B, S, f(tau), FAKE, o_dtype,
+                                      FAKE, FAKE, None)
+    assert p(Q=None) == RR_E_NULL
+    assert p(L=1004) == RR_E_SHAPE
+    assert p(tau=0.0) == RR_E_TAU
+    assert p(d=96) == RR_E_UNSUPPORTED
+    assert p(o_dtype=5) == RR_E_UNSUPPORTED
+    # 32K at 32/8 heads needs more than the 64 MiB array; 16K fits.
+    assert lib.rr_prefill_workspace_bytes(16384, 32, 8, 128, 128, 8) <= 64 << 20
+    assert lib.rr_prefill_workspace_bytes(32768, 32, 8, 128, 128, 8) > 64 << 20
+    assert p(L=32768, Hq=32, Hkv=8) == RR_E_WORKSPACE
+
+
 def test_select_and_attn_validation(lib):
     f = ctypes.c_float
     assert lib.rr_select(FAKE, 8, 1024, 128, f(0.0), FAKE, FAKE, None) == RR_E_TAU
