@@ -36,37 +36,52 @@ HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 
 
 CSRC = os.path.join(ROOT, "long_context_prefill_rr_amd", "csrc")
-ATTN_TRAFFIC = (os.path.join(ROOT, "profiles", "rr_block_sparse_fa_llama8b-128k_traffic.md"),
-                ["rr_attn.hip", "rr_device.h"])
-EST_TRAFFIC = (os.path.join(ROOT, "profiles", "rr_estimate_select_llama8b-128k_traffic.md"),
-               ["rr_estimate.hip", "rr_select.hip"])
-MFMA_BUSY = (os.path.join(ROOT, "profiles", "rr_block_sparse_fa_llama8b-128k_mfma_busy.md"),
-             ["rr_attn.hip", "rr_device.h"])
-MAT_TRAFFIC = (os.path.join(ROOT, "profiles", "rr_estimate_materialized_llama8b-128k_traffic.md"),
-               ["rr_estimate.hip", "rr_select.hip"])
+# Committed rocprofv3 summaries, one per workload (its name in the file
+# name), each valid for the kernel sources listed (sha256 in the file).
+# A workload's figures sit either in per-kernel summaries (the 128K
+# workload) or in one summary of all its kernels (rr_prefill_kernels_*.md,
+# which names the attention and estimation source hashes separately).
+_ATTN_SRC = ["rr_attn.hip", "rr_device.h"]
+_EST_SRC = ["rr_estimate.hip", "rr_select.hip"]
+ATTN_TRAFFIC = (["rr_block_sparse_fa_{}_traffic.md", "rr_prefill_kernels_{}.md"], _ATTN_SRC, "attn")
+EST_TRAFFIC = (["rr_estimate_select_{}_traffic.md", "rr_prefill_kernels_{}.md"], _EST_SRC, "est")
+MFMA_BUSY = (["rr_block_sparse_fa_{}_mfma_busy.md", "rr_prefill_kernels_{}.md"], _ATTN_SRC, "attn")
+MAT_TRAFFIC = (["rr_estimate_materialized_{}_traffic.md", "rr_prefill_kernels_{}.md"], _EST_SRC, "est",
+               "materialized_")   # field prefix in the all-kernel summaries
 
 
 def measured_traffic(workload_name, spec, field):
-    """Bytes per launch from a committed FETCH_SIZE / WRITE_SIZE summary, if it
-    was taken on the current kernel sources and on this workload; else None."""
+    """A figure (bytes per launch, kernel time, counter ratio) from the
+    committed rocprofv3 summary of this workload at its default S and tau, if
+    one exists and was taken on the current kernel sources; else None."""
     import hashlib
-    path, sources = spec
-    if workload_name != "llama8b-128k" or not os.path.exists(path):
+    if workload_name is None:
         return None
+    patterns, sources, kind = spec[:3]
+    combined_prefix = spec[3] if len(spec) > 3 else ""
     h = hashlib.sha256()
     for f in sources:
         h.update(open(os.path.join(CSRC, f), "rb").read())
-    fields = {}
-    for line in open(path):
-        if ":" in line and line.startswith("- "):
-            k, v = line[2:].split(":", 1)
-            fields[k.strip()] = v.strip().strip("`")
-    if fields.get("source_sha256") != h.hexdigest():
-        return None
-    try:
-        return float(fields[field])
-    except (KeyError, ValueError):
-        return None
+    for pattern in patterns:
+        path = os.path.join(ROOT, "profiles", pattern.format(workload_name))
+        if not os.path.exists(path):
+            continue
+        fields = {}
+        for line in open(path):
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+        name = field
+        if "%s_source_sha256" % kind in fields:      # an all-kernel summary
+            name = combined_prefix + field
+        sha = fields.get("%s_source_sha256" % kind, fields.get("source_sha256"))
+        if sha != h.hexdigest() or name not in fields:
+            continue
+        try:
+            return float(fields[name])
+        except ValueError:
+            return None
+    return None
 
 
 def log(msg):
@@ -454,13 +469,15 @@ def main():
     design_a_bytes = (L * Hkv * d * 2 + ns_ * Hq * d * 2 + 2 * ns_ * Hkv * d * 4
                       + 2 * Hq * c_ * c_ * (nb * (nb + 1) // 2) * 4 + 2 * Hq * nb * nb * 4
                       + Hq * nb * nb * 4)
-    est_traffic = measured_traffic(w.name, EST_TRAFFIC, "traffic_bytes_per_step")
+    # Counter summaries describe the workload at its default S and tau only.
+    prof_name = w.name if (args.S is None and args.tau is None) else None
+    est_traffic = measured_traffic(prof_name, EST_TRAFFIC, "traffic_bytes_per_step")
     # The estimation's matrix work: every sampled row (Hq heads x ns strides)
     # against every pooled key j <= i, over the three bf16 planes of the
     # pooled key (3 d-long products, 2 FLOP per multiply-add).
     score_flops = 3.0 * 2.0 * d * Hq * ns_ * (ns_ + 1) / 2.0
     est_ms = float(est.mean())
-    score_kernel_us = measured_traffic(w.name, EST_TRAFFIC, "score_kernel_avg_us")
+    score_kernel_us = measured_traffic(prof_name, EST_TRAFFIC, "score_kernel_avg_us")
     score_roofline = {
         "kernel": "rr_score32 (sampled rows x pooled keys, three bf16 planes)", "bound": "mfma",
         "unit": "TFLOP/s", "peak": MFMA_BF16_PEAK_TFLOPS, "flops_per_launch": score_flops,
@@ -472,7 +489,7 @@ def main():
         "frac_kernel_rocprof": None if score_kernel_us is None
         else score_flops / (score_kernel_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
     if materialized is not None:
-        mt = measured_traffic(w.name, MAT_TRAFFIC, "traffic_bytes_per_step")
+        mt = measured_traffic(prof_name, MAT_TRAFFIC, "traffic_bytes_per_step")
         mms = materialized["ms"]
         materialized.update({
             "design_a_bytes": design_a_bytes,
@@ -531,12 +548,12 @@ def main():
                     "materialized": materialized},
         "roofline": {"kernel": "rr_block_sparse_fa (with its V transpose)", "bound": "mfma",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic(w.name, ATTN_TRAFFIC, "traffic_bytes_per_launch"),
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic(prof_name, ATTN_TRAFFIC, "traffic_bytes_per_launch"),
                      "flops_per_launch": flops_kept,
                      # rocprof counters of this kernel (committed summary, same sources):
                      # matrix-unit busy cycles over all SIMD cycles, and the clock it ran at.
-                     "mfma_busy_counter": measured_traffic(w.name, MFMA_BUSY, "mfma_busy_frac"),
-                     "clock_ghz_under_load": measured_traffic(w.name, MFMA_BUSY, "clock_ghz")},
+                     "mfma_busy_counter": measured_traffic(prof_name, MFMA_BUSY, "mfma_busy_frac"),
+                     "clock_ghz_under_load": measured_traffic(prof_name, MFMA_BUSY, "clock_ghz")},
     }
     if args.cpu_baseline == "on":
         log("cpu baseline (oracle) on a sample ...")
