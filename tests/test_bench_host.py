@@ -40,11 +40,28 @@ def test_kept_block_flops_counts_causal_pairs():
 
 
 def test_traffic_summary_requires_matching_source(tmp_path):
+    import hashlib
     b = _bench()
-    path = tmp_path / "t.md"
-    path.write_text("- source_sha256: `0000`\n- traffic_bytes_per_launch: 123\n")
-    spec = (str(path), ["rr_attn.hip"])
-    assert b.measured_traffic("llama8b-128k", spec, "traffic_bytes_per_launch") is None
-    assert b.measured_traffic("llama8b-8k", b.ATTN_TRAFFIC, "traffic_bytes_per_launch") is None
+    src = open(os.path.join(b.CSRC, "rr_attn.hip"), "rb").read()
+    good = hashlib.sha256(src).hexdigest()
+    path = tmp_path / "t_{}.md"
+    # a per-kernel summary: one source hash
+    (tmp_path / "t_wl.md").write_text("- source_sha256: `0000`\n- traffic_bytes_per_launch: 123\n")
+    spec = ([str(path)], ["rr_attn.hip"], "attn")
+    assert b.measured_traffic("wl", spec, "traffic_bytes_per_launch") is None      # stale hash
+    (tmp_path / "t_wl.md").write_text("- source_sha256: `%s`\n- traffic_bytes_per_launch: 123\n" % good)
+    assert b.measured_traffic("wl", spec, "traffic_bytes_per_launch") == 123.0
+    assert b.measured_traffic("wl", spec, "other_field") is None
+    assert b.measured_traffic(None, spec, "traffic_bytes_per_launch") is None       # non-default S / tau
+    # an all-kernel summary: per-kind hashes, and a field prefix for the materialised figures
+    (tmp_path / "t_wl.md").write_text("- attn_source_sha256: `%s`\n- est_source_sha256: `0000`\n"
+                                      "- traffic_bytes_per_step: 7\n- materialized_traffic_bytes_per_step: 9\n"
+                                      % good)
+    assert b.measured_traffic("wl", ([str(path)], ["rr_attn.hip"], "attn"), "traffic_bytes_per_step") == 7.0
+    assert b.measured_traffic("wl", ([str(path)], ["rr_attn.hip"], "attn", "materialized_"),
+                              "traffic_bytes_per_step") == 9.0
+    assert b.measured_traffic("wl", ([str(path)], ["rr_attn.hip"], "est"), "traffic_bytes_per_step") is None
+    # committed summaries
+    assert b.measured_traffic("no-such-workload", b.ATTN_TRAFFIC, "traffic_bytes_per_launch") is None
     got = b.measured_traffic("llama8b-128k", b.ATTN_TRAFFIC, "traffic_bytes_per_launch")
     assert got is None or got > 1e9
