@@ -56,8 +56,9 @@ int run_attn(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const Shap
              const int32_t *counts, const int32_t *block_idx, void *O, int o_dtype, void *ws,
              hipStream_t st) {
     uint16_t *Vt = (uint16_t *)ws;
-    if (launch_transpose_v(V, s, Vt, st) != hipSuccess) return RR_E_HIP;
-    if (launch_block_sparse_fa(Q, K, Vt, s, counts, block_idx, O, o_dtype == RR_OUT_F32, st) !=
+    unsigned *counter = (unsigned *)((char *)ws + attn_vt_bytes(s));
+    if (launch_transpose_v(V, s, Vt, counter, st) != hipSuccess) return RR_E_HIP;
+    if (launch_block_sparse_fa(Q, K, Vt, counter, s, counts, block_idx, O, o_dtype == RR_OUT_F32, st) !=
         hipSuccess)
         return RR_E_HIP;
     return RR_OK;

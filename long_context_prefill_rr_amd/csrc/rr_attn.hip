@@ -32,11 +32,14 @@
 // O^T stays in registers (one query column per lane) and is divided by the
 // softmax sum at the end.
 //
-// Grid order: kv-head major, block-row descending, the head pairs of one
-// (g, I) adjacent and on the same XCD (work-groups are dealt to the 8 XCDs
-// round-robin), so the K/V tiles they share are served from that XCD's L2
-// and one kv-head's K/V (64 MiB at 128K) stays in the last-level cache while
-// its rows run; long rows start first.
+// Work order: each work-group takes the next item from a device counter
+// (reset by rr_transpose_v, which runs just before on the same stream), in
+// the order kv-head major, block-row descending, head pairs of one (g, I)
+// adjacent: long rows start first, one kv-head's K/V (64 MiB at 128K) stays
+// in the last-level cache while its rows run, and an XCD whose work-groups
+// finish early simply takes more items.  (Work-groups are dealt to the 8
+// XCDs by block index; a fixed mapping from block index to rows left the
+// XCDs with up to 41% different work on the 64K video shape.)
 #include "rr_device.h"
 #include "rr_internal.h"
 
@@ -46,10 +49,13 @@ namespace rr {
 constexpr int KLA = 2;
 
 // V [L][Hkv][d] -> Vt [Hkv][d][Lp], tokens >= L zero-filled.  64x64 tiles.
+// Also resets the attention kernel's work counter.
 __global__ __launch_bounds__(256) void rr_transpose_v(const uint16_t *__restrict__ V, int L, int Lp,
-                                                      int Hkv, int D, uint16_t *__restrict__ Vt) {
+                                                      int Hkv, int D, uint16_t *__restrict__ Vt,
+                                                      unsigned *__restrict__ counter) {
     __shared__ uint16_t tile[64][66];
     const int t0 = blockIdx.x * 64, d0 = blockIdx.y * 64, g = blockIdx.z;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *counter = 0u;
     for (int i = threadIdx.x; i < 64 * 32; i += 256) {
         const int r = i >> 5, c2 = (i & 31) * 2;
         const int t = t0 + r;
@@ -124,8 +130,9 @@ __device__ __forceinline__ float sum_halves(float x) {
 template <int D, int BLK, bool OUT_F32>
 __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_fa(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ Vt,
-    int L, int Lp, int Hq, int Hkv, int nb, int nq, const int32_t *__restrict__ counts,
-    const int32_t *__restrict__ block_idx, void *__restrict__ O, float scale2) {
+    unsigned *__restrict__ counter, int L, int Lp, int Hq, int Hkv, int nb, int nq,
+    const int32_t *__restrict__ counts, const int32_t *__restrict__ block_idx, void *__restrict__ O,
+    float scale2) {
     using C = FaCfg<D, BLK>;
     __shared__ __attribute__((aligned(1024))) char Kb0[C::KBYTES];
     __shared__ __attribute__((aligned(1024))) char Kb1[C::KBYTES];
@@ -142,18 +149,16 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
 
     const int G = Hq / Hkv;
     const int npair = (G + 1) >> 1;
-    // Work decode: (kv-head g, block-row I) pairs qi in kv-head-major order
-    // with I descending, times head pairs.  Work-groups are dealt to the 8
-    // XCDs round-robin, so XCD x runs bx = x, x+8, ...: its slot-th work-group
-    // gets pair qi = (slot / npair)*8 + x and head pair slot % npair.  The 8
-    // XCDs work on neighbouring block-rows of one kv-head at a time (their
-    // K/V tiles meet in the shared last-level cache) and the head pairs of
-    // one row stay on one XCD (sharing its L2).
-    const int bx = blockIdx.x;
-    const int x = bx & 7, slot = bx >> 3;
-    const int pp = slot % npair;
-    const int qi = (slot / npair) * 8 + x;
-    if (qi >= nq) return;
+    // Work item: (kv-head g, block-row I) index qi in kv-head-major order
+    // with I descending, times head pairs; the grid has exactly one
+    // work-group per item and each takes the next one from the counter.
+    __shared__ int item_sh;
+    if (threadIdx.x == 0) item_sh = (int)atomicAdd(counter, 1u);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(item_sh);
+    const int pp = item % npair;
+    const int qi = item / npair;
+    if (qi >= nq) return;   // not reached: the grid has nq * npair work-groups
     const int g = qi / nb;
     const int I = nb - 1 - qi % nb;
 
@@ -268,32 +273,20 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
     const char *kbase = reinterpret_cast<const char *>(K + (size_t)g * D);
     const char *vbase = reinterpret_cast<const char *>(Vt + (size_t)g * D * Lp);
 
-    // Start the copies of stage st (key block J) into (kb, vb).
+    // Start the copies of stage st (key block J) into (kb, vb).  The K
+    // resource is based at the stage's first key row and ends after key row
+    // L-1: the rows of a short last stage past L are read as zeros (their
+    // scores are masked causally).  V^T is zero-padded to Lp.
     auto issue = [&](int st, char *kb, char *vb) {
         st = copy_stage(st);
         const int ent = __builtin_amdgcn_readfirstlane((int)ulist[st / C::SPB]);
         const int J = ent & 0xffff;
         const int key0 = J * BLK + (st % C::SPB) * C::KT;
-        const bool full = key0 + C::KT <= L;
-        // Buffer resources based at this stage's first K row (clamped to row
-        // L-1 for a stage that starts at or past L) and first V^T column;
-        // each lane adds its byte offset.
-        const int krow0 = full ? key0 : min(key0, L - 1);
-        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kbase + (size_t)krow0 * Hkv * D * 2);
+        const __amdgpu_buffer_rsrc_t rk =
+            buf_rsrc_n(kbase + (size_t)key0 * Hkv * D * 2, max(L - key0, 0) * Hkv * D * 2);
         const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vbase + (size_t)key0 * 2);
 #pragma unroll
-        for (int i = 0; i < C::IK; ++i) {
-            uint32_t off = koff[i];
-            if (!full) {
-                // Short last stage: rows past L re-read row L-1 (masked later).
-                // krow0 <= min(key0 + r, L - 1), so the offset is not negative.
-                const int p = (wid * C::IK + i) * 64 + lane;
-                const int r = p / C::CPRK, c = (p % C::CPRK) ^ swz_k<D>(r);
-                const int rr = min(key0 + r, L - 1) - krow0;
-                off = (uint32_t)((rr * Hkv * D + c * 8) * 2);
-            }
-            buf2lds16(rk, off, (lds_char *)kb + (wid * C::IK + i) * 1024);
-        }
+        for (int i = 0; i < C::IK; ++i) buf2lds16(rk, koff[i], (lds_char *)kb + (wid * C::IK + i) * 1024);
 #pragma unroll
         for (int i = 0; i < C::IV; ++i) buf2lds16(rv, voff[i], (lds_char *)vb + (wid * C::IV + i) * 1024);
     };
@@ -456,41 +449,41 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
     }
 }
 
-hipError_t launch_transpose_v(const uint16_t *V, const Shape &s, uint16_t *Vt, hipStream_t st) {
+hipError_t launch_transpose_v(const uint16_t *V, const Shape &s, uint16_t *Vt, unsigned *counter,
+                              hipStream_t st) {
     const int Lp = s.nb * s.B;
     hipLaunchKernelGGL(rr_transpose_v, dim3(Lp / 64, s.d / 64, s.Hkv), dim3(256), 0, st, V, s.L, Lp,
-                       s.Hkv, s.d, Vt);
+                       s.Hkv, s.d, Vt, counter);
     return hipGetLastError();
 }
 
 template <int D, int BLK>
-static void launch_fa_t(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, const Shape &s,
-                        const int32_t *counts, const int32_t *block_idx, void *O, bool out_f32,
-                        hipStream_t st) {
+static void launch_fa_t(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, unsigned *counter,
+                        const Shape &s, const int32_t *counts, const int32_t *block_idx, void *O,
+                        bool out_f32, hipStream_t st) {
     const int nq = s.nb * s.Hkv;
-    const int nq8 = (nq + 7) / 8 * 8;
-    const dim3 grid((unsigned)(nq8 * ((s.G + 1) / 2)));
+    const dim3 grid((unsigned)(nq * ((s.G + 1) / 2)));   // one work-group per work item
     const float scale2 = kLog2e / sqrtf((float)D);
     const int Lp = s.nb * BLK;
     if (out_f32)
         hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true>), grid, dim3(BLK * 4), 0, st, Q, K, Vt,
-                           s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O, scale2);
+                           counter, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O, scale2);
     else
         hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false>), grid, dim3(BLK * 4), 0, st, Q, K,
-                           Vt, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O, scale2);
+                           Vt, counter, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O, scale2);
 }
 
 hipError_t launch_block_sparse_fa(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt,
-                                  const Shape &s, const int32_t *counts, const int32_t *block_idx,
-                                  void *O, bool out_f32, hipStream_t st) {
+                                  unsigned *counter, const Shape &s, const int32_t *counts,
+                                  const int32_t *block_idx, void *O, bool out_f32, hipStream_t st) {
     if (s.d == 128 && s.B == 128)
-        launch_fa_t<128, 128>(Q, K, Vt, s, counts, block_idx, O, out_f32, st);
+        launch_fa_t<128, 128>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
     else if (s.d == 128 && s.B == 64)
-        launch_fa_t<128, 64>(Q, K, Vt, s, counts, block_idx, O, out_f32, st);
+        launch_fa_t<128, 64>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
     else if (s.d == 64 && s.B == 128)
-        launch_fa_t<64, 128>(Q, K, Vt, s, counts, block_idx, O, out_f32, st);
+        launch_fa_t<64, 128>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
     else
-        launch_fa_t<64, 64>(Q, K, Vt, s, counts, block_idx, O, out_f32, st);
+        launch_fa_t<64, 64>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
     return hipGetLastError();
 }
 

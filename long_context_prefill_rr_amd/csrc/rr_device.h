@@ -79,6 +79,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, -1, kBufFlags);
 }
 
+// Buffer resource over the first `bytes` bytes starting at p: a load whose
+// byte offset lies at or past `bytes` returns zeros (no memory access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc_n(const void *p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, kBufFlags);
+}
+
 // 16-byte buffer -> LDS copy without registers (buffer_load_dwordx4 ... lds):
 // lane i reads rsrc base + off and writes lds_wave_base + 16*i.  Unlike the
 // flat-encoded global_load_lds, a buffer copy in flight leaves the compiler

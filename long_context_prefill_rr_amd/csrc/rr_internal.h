@@ -63,8 +63,11 @@ inline EstimateWs carve_estimate(const Shape &s, void *ws) {
 // owns c rows of (I+1)c strides, i.e. c * P floats in all.
 inline long long score_elems_per_head(const Shape &s) { return (long long)s.c * s.P; }
 
-// Attention workspace: V transposed to [Hkv][d][nb*B] (zero-padded tail).
-inline size_t attn_ws_bytes(const Shape &s) { return align_up((size_t)s.Hkv * s.d * s.nb * s.B * 2); }
+// Attention workspace: V transposed to [Hkv][d][nb*B] (zero-padded tail),
+// then the work counter of the attention kernel (one 32-bit word in its own
+// 256-byte slot).
+inline size_t attn_vt_bytes(const Shape &s) { return align_up((size_t)s.Hkv * s.d * s.nb * s.B * 2); }
+inline size_t attn_ws_bytes(const Shape &s) { return attn_vt_bytes(s) + kAlign; }
 
 // rr_prefill's host-side argument checks (everything but the workspace) and
 // its launch sequence on a workspace of at least rr_prefill_workspace_bytes;
@@ -85,8 +88,10 @@ hipError_t launch_score_store(const uint16_t *Q, const Shape &s, const EstimateW
 hipError_t launch_pool_scores(const Shape &s, const float *scores, float *A, hipStream_t st);
 hipError_t launch_topk_tau(const float *A, const Shape &s, float tau, int32_t *counts,
                            int32_t *block_idx, hipStream_t st);
-hipError_t launch_transpose_v(const uint16_t *V, const Shape &s, uint16_t *Vt, hipStream_t st);
+hipError_t launch_transpose_v(const uint16_t *V, const Shape &s, uint16_t *Vt, unsigned *counter,
+                              hipStream_t st);
 hipError_t launch_block_sparse_fa(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt,
+                                  unsigned *counter,
                                   const Shape &s, const int32_t *counts, const int32_t *block_idx,
                                   void *O, bool out_f32, hipStream_t st);
 hipError_t launch_xscore(const uint16_t *Q, const uint16_t *K, const Shape &s, bool average,
