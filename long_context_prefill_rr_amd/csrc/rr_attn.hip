@@ -32,14 +32,18 @@
 // O^T stays in registers (one query column per lane) and is divided by the
 // softmax sum at the end.
 //
-// Work order: each work-group takes the next item from a device counter
-// (reset by rr_transpose_v, which runs just before on the same stream), in
-// the order kv-head major, block-row descending, head pairs of one (g, I)
-// adjacent: long rows start first, one kv-head's K/V (64 MiB at 128K) stays
-// in the last-level cache while its rows run, and an XCD whose work-groups
-// finish early simply takes more items.  (Work-groups are dealt to the 8
+// Work order: work-groups take items from a device counter (reset by
+// rr_transpose_v, which runs just before on the same stream), in the order
+// kv-head major, block-row descending, head pairs of one (g, I) adjacent:
+// long rows start first, one kv-head's K/V (64 MiB at 128K) stays in the
+// last-level cache while its rows run, and a CU that finishes an item early
+// simply takes the next.  Up to 512 blocks the work-groups are persistent
+// (one per CU, looping over items), so none is launched or torn down
+// between the short items.  (Work-groups are dealt to the 8
 // XCDs by block index; a fixed mapping from block index to rows left the
 // XCDs with up to 41% different work on the 64K video shape.)
+#include <algorithm>
+
 #include "rr_device.h"
 #include "rr_internal.h"
 
@@ -127,10 +131,15 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 // A 64-row block makes a 4-wave work-group that fits once per CU (LDS): one
 // wave per SIMD.
-template <int D, int BLK, bool OUT_F32>
+//
+// PERSIST: the grid holds about one work-group per CU and each loops over work
+// items; otherwise the grid holds one work-group per item (the loop body runs
+// once).  The loop costs registers, and at long rows (nb > 512) the launch of
+// a new work-group per item is a smaller cost than that.
+template <int D, int BLK, bool OUT_F32, bool PERSIST>
 __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_fa(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ Vt,
-    unsigned *__restrict__ counter, int L, int Lp, int Hq, int Hkv, int nb, int nq,
+    unsigned *__restrict__ counter, int nitems, int L, int Lp, int Hq, int Hkv, int nb, int nq,
     const int32_t *__restrict__ counts, const int32_t *__restrict__ block_idx, void *__restrict__ O,
     float scale2) {
     using C = FaCfg<D, BLK>;
@@ -149,19 +158,6 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
 
     const int G = Hq / Hkv;
     const int npair = (G + 1) >> 1;
-    // Work item: (kv-head g, block-row I) index qi in kv-head-major order
-    // with I descending, times head pairs; the grid has exactly one
-    // work-group per item and each takes the next one from the counter.
-    __shared__ int item_sh;
-    if (threadIdx.x == 0) item_sh = (int)atomicAdd(counter, 1u);
-    __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(item_sh);
-    const int pp = item % npair;
-    const int qi = item / npair;
-    if (qi >= nq) return;   // not reached: the grid has nq * npair work-groups
-    const int g = qi / nb;
-    const int I = nb - 1 - qi % nb;
-
     const int tid = threadIdx.x;
     // The wave index is uniform: readfirstlane lets the compiler keep it and
     // everything derived from it (LDS copy bases, head group) in SGPRs.
@@ -169,6 +165,22 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
     const int gr = wid / C::NWG;              // head group of this wave
     const int rw = wid % C::NWG;              // 32-row tile of this wave
     const int col = lane & 31, hk = lane >> 5;
+
+    // Work items come from the counter until they run out (PERSIST), or one
+    // per work-group.  Item = (kv-head g, block-row I) index qi in
+    // kv-head-major order with I descending, times head pairs.  Every wave of
+    // the work-group reads the same item, so all leave together.
+    __shared__ int item_sh;
+    for (;;) {
+    __syncthreads();   // every wave is done with the previous item's LDS
+    if (tid == 0) item_sh = (int)atomicAdd(counter, 1u);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(item_sh);
+    if (item >= nitems) break;
+    const int pp = item % npair;
+    const int qi = item / npair;
+    const int g = qi / nb;
+    const int I = nb - 1 - qi % nb;
     const bool head_ok = 2 * pp + gr < G;     // odd G: the last pair has one head
     const int h = g * G + min(2 * pp + gr, G - 1);
     const int tq = I * BLK + rw * 32 + col;
@@ -430,23 +442,26 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
 
     const float tot = sum_halves(lsum);
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
-    if (tq >= L || !head_ok) return;
+    if (tq < L && head_ok) {
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) {
+        for (int dt = 0; dt < C::NDT; ++dt) {
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            const int d0 = dt * 32 + 8 * e4 + 4 * hk;
-            const float v0 = o[dt][4 * e4] * inv, v1 = o[dt][4 * e4 + 1] * inv;
-            const float v2 = o[dt][4 * e4 + 2] * inv, v3 = o[dt][4 * e4 + 3] * inv;
-            if constexpr (OUT_F32) {
-                float *op = reinterpret_cast<float *>(O) + ((size_t)tq * Hq + h) * D + d0;
-                *reinterpret_cast<float4 *>(op) = make_float4(v0, v1, v2, v3);
-            } else {
-                uint16_t *op = reinterpret_cast<uint16_t *>(O) + ((size_t)tq * Hq + h) * D + d0;
-                *reinterpret_cast<uint2 *>(op) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int d0 = dt * 32 + 8 * e4 + 4 * hk;
+                const float v0 = o[dt][4 * e4] * inv, v1 = o[dt][4 * e4 + 1] * inv;
+                const float v2 = o[dt][4 * e4 + 2] * inv, v3 = o[dt][4 * e4 + 3] * inv;
+                if constexpr (OUT_F32) {
+                    float *op = reinterpret_cast<float *>(O) + ((size_t)tq * Hq + h) * D + d0;
+                    *reinterpret_cast<float4 *>(op) = make_float4(v0, v1, v2, v3);
+                } else {
+                    uint16_t *op = reinterpret_cast<uint16_t *>(O) + ((size_t)tq * Hq + h) * D + d0;
+                    *reinterpret_cast<uint2 *>(op) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+                }
             }
         }
     }
+    if constexpr (!PERSIST) break;
+    }  // work items
 }
 
 hipError_t launch_transpose_v(const uint16_t *V, const Shape &s, uint16_t *Vt, unsigned *counter,
@@ -457,20 +472,54 @@ hipError_t launch_transpose_v(const uint16_t *V, const Shape &s, uint16_t *Vt, u
     return hipGetLastError();
 }
 
+// Longest block count for which the persistent form is launched.
+constexpr int kPersistMaxNb = 512;
+
+// Compute units of the current device (queried once per device).
+static int device_cu_count() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 template <int D, int BLK>
 static void launch_fa_t(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, unsigned *counter,
                         const Shape &s, const int32_t *counts, const int32_t *block_idx, void *O,
                         bool out_f32, hipStream_t st) {
     const int nq = s.nb * s.Hkv;
-    const dim3 grid((unsigned)(nq * ((s.G + 1) / 2)));   // one work-group per work item
+    const int nitems = nq * ((s.G + 1) / 2);
     const float scale2 = kLog2e / sqrtf((float)D);
     const int Lp = s.nb * BLK;
-    if (out_f32)
-        hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true>), grid, dim3(BLK * 4), 0, st, Q, K, Vt,
-                           counter, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O, scale2);
-    else
-        hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false>), grid, dim3(BLK * 4), 0, st, Q, K,
-                           Vt, counter, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O, scale2);
+    const dim3 block(BLK * 4);
+    if (s.nb <= kPersistMaxNb) {
+        // One persistent work-group per CU (each holds most of a CU's LDS).
+        const dim3 grid((unsigned)std::min(nitems, device_cu_count()));
+        if (out_f32)
+            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true, true>), grid, block, 0, st, Q, K, Vt,
+                               counter, nitems, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O,
+                               scale2);
+        else
+            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false, true>), grid, block, 0, st, Q, K, Vt,
+                               counter, nitems, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O,
+                               scale2);
+    } else {
+        const dim3 grid((unsigned)nitems);
+        if (out_f32)
+            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true, false>), grid, block, 0, st, Q, K,
+                               Vt, counter, nitems, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts,
+                               block_idx, O, scale2);
+        else
+            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false, false>), grid, block, 0, st, Q, K,
+                               Vt, counter, nitems, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts,
+                               block_idx, O, scale2);
+    }
 }
 
 hipError_t launch_block_sparse_fa(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt,
