@@ -33,15 +33,15 @@
 // softmax sum at the end.
 //
 // Work order: work-groups take items from a device counter (reset by
-// rr_transpose_v, which runs just before on the same stream), in the order
-// kv-head major, block-row descending, head pairs of one (g, I) adjacent:
-// long rows start first, one kv-head's K/V (64 MiB at 128K) stays in the
-// last-level cache while its rows run, and a CU that finishes an item early
-// simply takes the next.  Up to 512 blocks the work-groups are persistent
-// (one per CU, looping over items), so none is launched or torn down
-// between the short items.  (Work-groups are dealt to the 8
-// XCDs by block index; a fixed mapping from block index to rows left the
-// XCDs with up to 41% different work on the 64K video shape.)
+// rr_transpose_v, which runs just before on the same stream), ordered
+// block-row descending within one kv-head at a time (all kv-heads together
+// when each CU takes at most 8 items), then kv-head and head pair: long rows
+// start first, the K/V in use stays in the last-level cache, and a CU that
+// finishes an item early simply takes the next.  Up to 512 blocks the
+// work-groups are persistent (one per CU, looping over items), so none is
+// launched or torn down between the short items.  (Work-groups are dealt to
+// the 8 XCDs by block index; a fixed mapping from block index to rows left
+// the XCDs with up to 41% different work on the 64K video shape.)
 #include <algorithm>
 
 #include "rr_device.h"
@@ -139,7 +139,8 @@ __device__ __forceinline__ float sum_halves(float x) {
 template <int D, int BLK, bool OUT_F32, bool PERSIST>
 __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_fa(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ Vt,
-    unsigned *__restrict__ counter, int nitems, int L, int Lp, int Hq, int Hkv, int nb, int nq,
+    unsigned *__restrict__ counter, int nitems, int hchunk, int L, int Lp, int Hq, int Hkv, int nb,
+    int nq,
     const int32_t *__restrict__ counts, const int32_t *__restrict__ block_idx, void *__restrict__ O,
     float scale2) {
     using C = FaCfg<D, BLK>;
@@ -167,9 +168,11 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
     const int col = lane & 31, hk = lane >> 5;
 
     // Work items come from the counter until they run out (PERSIST), or one
-    // per work-group.  Item = (kv-head g, block-row I) index qi in
-    // kv-head-major order with I descending, times head pairs.  Every wave of
-    // the work-group reads the same item, so all leave together.
+    // per work-group.  Items are ordered by chunks of hchunk kv-heads (one,
+    // or all of them when there are few items per CU), then block-row
+    // descending, then kv-head, then head pair, so the longest rows of every
+    // kv-head of a chunk start first.  Every wave of the work-group
+    // reads the same item, so all leave together.
     __shared__ int item_sh;
     for (;;) {
     __syncthreads();   // every wave is done with the previous item's LDS
@@ -177,10 +180,12 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(item_sh);
     if (item >= nitems) break;
-    const int pp = item % npair;
-    const int qi = item / npair;
-    const int g = qi / nb;
-    const int I = nb - 1 - qi % nb;
+    const int per_chunk = hchunk * nb * npair;
+    const int c_ = item / per_chunk, r_ = item - c_ * per_chunk;
+    const int I = nb - 1 - r_ / (hchunk * npair);
+    const int r2 = r_ % (hchunk * npair);
+    const int g = c_ * hchunk + r2 / npair;
+    const int pp = r2 % npair;
     const bool head_ok = 2 * pp + gr < G;     // odd G: the last pair has one head
     const int h = g * G + min(2 * pp + gr, G - 1);
     const int tq = I * BLK + rw * 32 + col;
@@ -474,6 +479,13 @@ hipError_t launch_transpose_v(const uint16_t *V, const Shape &s, uint16_t *Vt, u
 
 // Longest block count for which the persistent form is launched.
 constexpr int kPersistMaxNb = 512;
+// Items per CU up to which the items of all kv-heads are interleaved
+// (block-rows descending over every kv-head: the longest rows start first,
+// which matters when each CU takes only a few items).  With more items per
+// CU one kv-head at a time keeps the K/V in use small: interleaving two
+// kv-heads measured 8% slower at 128K and 2.5% slower at 32K, all eight 10%
+// faster at 8K (4 items per CU).
+constexpr int kInterleaveMaxItemsPerCu = 8;
 
 // Compute units of the current device (queried once per device).
 static int device_cu_count() {
@@ -495,29 +507,33 @@ static void launch_fa_t(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt
                         bool out_f32, hipStream_t st) {
     const int nq = s.nb * s.Hkv;
     const int nitems = nq * ((s.G + 1) / 2);
+    // kv-heads per chunk of the item order: all of them for few items per
+    // CU, else one.
+    const int ncu = device_cu_count();
+    const int hchunk = nitems <= kInterleaveMaxItemsPerCu * ncu ? s.Hkv : 1;
     const float scale2 = kLog2e / sqrtf((float)D);
     const int Lp = s.nb * BLK;
     const dim3 block(BLK * 4);
     if (s.nb <= kPersistMaxNb) {
         // One persistent work-group per CU (each holds most of a CU's LDS).
-        const dim3 grid((unsigned)std::min(nitems, device_cu_count()));
+        const dim3 grid((unsigned)std::min(nitems, ncu));
         if (out_f32)
             hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true, true>), grid, block, 0, st, Q, K, Vt,
-                               counter, nitems, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O,
+                               counter, nitems, hchunk, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O,
                                scale2);
         else
             hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false, true>), grid, block, 0, st, Q, K, Vt,
-                               counter, nitems, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O,
+                               counter, nitems, hchunk, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O,
                                scale2);
     } else {
         const dim3 grid((unsigned)nitems);
         if (out_f32)
             hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true, false>), grid, block, 0, st, Q, K,
-                               Vt, counter, nitems, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts,
+                               Vt, counter, nitems, hchunk, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts,
                                block_idx, O, scale2);
         else
             hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false, false>), grid, block, 0, st, Q, K,
-                               Vt, counter, nitems, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts,
+                               Vt, counter, nitems, hchunk, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts,
                                block_idx, O, scale2);
     }
 }
