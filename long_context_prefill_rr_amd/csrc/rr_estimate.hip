@@ -28,6 +28,7 @@
 // separate MFMA pass with fp32 accumulation.  Scores live in the log2 domain
 // (scaled by log2(e)/sqrt(d)) so exponentials are single v_exp_f32.
 #include <algorithm>
+#include <type_traits>
 
 #include "rr_device.h"
 #include "rr_internal.h"
@@ -362,20 +363,33 @@ __global__ __launch_bounds__(256) void rr_score(const uint16_t *__restrict__ Q,
 }
 
 // ---------------------------------------------------------------------------
-// rr_score32: rr_score's work split, rows and outputs for blocks of 4, 8 or
-// 16 strides, with 32 x 32 tiles on v_mfma_f32_32x32x16_bf16.  The pooled-key
-// rows fed to the matrix unit are permuted so that accumulator register e of
-// lane (row q, half) holds stride 16*half + e of the 32-stride unit: a lane
-// owns whole key blocks of its row, and each block's max and sum of
-// exponentials are taken in registers with no cross-lane step (the 16-stride
-// tiles of rr_score spread a block over four lanes).  The waves take units
-// wid, wid+4, ...; a unit's pooled-key fragments (3 planes x d/16 steps) stay
-// in registers across the work-group's row tiles, and during the last row
-// tile each step's fragments are reloaded with the next unit's once that
-// step's products are issued.
+// rr_score32: rr_score's rows and outputs for blocks of 4, 8 or 16 strides,
+// with 32 x 32 tiles on v_mfma_f32_32x32x16_bf16.  The pooled-key rows fed
+// to the matrix unit are permuted so that accumulator register e of lane
+// (row q, half) holds stride 16*half + e of the 32-stride unit: a lane owns
+// whole key blocks of its row, and each block's max and sum of exponentials
+// are taken in registers with no cross-lane step (the 16-stride tiles of
+// rr_score spread a block over four lanes).
+//
+// The four waves walk the 32-stride units 0, 1, ... together, and wave w
+// owns row tiles 2w and 2w+1 for the whole pass: their Q fragments stay in
+// registers, and every pooled-key fragment read from LDS feeds the products
+// of both tiles (two independent accumulation chains).  Each unit's three
+// planes (32 strides x d) are copied global -> LDS by the work-group
+// (buffer_load ... lds, no registers) one unit ahead, into one of two
+// buffers; rows past the last stride read as zeros and are masked causally.
+// A wave whose rows all end before a unit only copies and waits for it.
 // ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int score_swz(int r) {
+    // 16-byte slot XOR per pooled-key row: the 16 rows one 16-lane group
+    // reads for one fragment fall in 16 distinct bank groups.
+    if constexpr (D == 128) return (r & 7) | (((r >> 4) & 1) << 3);
+    else return ((r >> 1) & 3) | (((r >> 4) & 1) << 2);
+}
+
 template <int D, int C>
-__global__ __launch_bounds__(256, 2) void rr_score32(const uint16_t *__restrict__ Q,
+__global__ __launch_bounds__(256, 3) void rr_score32(const uint16_t *__restrict__ Q,
                                                      const uint16_t *__restrict__ Kp, int Hq, int Hkv,
                                                      int S, int nb, int ns, int G, int R, int nchunks,
                                                      long long P, float scale2,
@@ -383,13 +397,18 @@ __global__ __launch_bounds__(256, 2) void rr_score32(const uint16_t *__restrict_
                                                      float2 *__restrict__ rowstat) {
     static_assert(C == 4 || C == 8 || C == 16, "blocks of 4, 8 or 16 strides");
     constexpr int NKS = D / 16;                // 16-wide contraction steps
-    constexpr int CPR = D / 8;                 // 16-byte chunks per Q row
-    constexpr int MT = kScoreRows / 32;        // row tiles per work-group
+    constexpr int CPR = D / 8;                 // 16-byte chunks per row
     constexpr int BPL = 16 / C;                // key blocks per lane per unit
-    __shared__ __attribute__((aligned(16))) uint16_t qs[kScoreRows * D];
-    __shared__ float2 red[4][kScoreRows];
+    constexpr int PLANE_B = 32 * D * 2;        // one plane of a unit in LDS
+    constexpr int UNIT_B = 3 * PLANE_B;
+    constexpr int CPW = UNIT_B / (4 * 1024);   // 1 KiB copies per wave per unit
+    constexpr int CPP = PLANE_B / 1024;        // copies per plane
+    static_assert(CPW * 4 * 1024 == UNIT_B && CPP * 1024 == PLANE_B, "whole copies");
+    constexpr int LA = 1;                      // fragment look-ahead (steps): 160 VGPRs, 3 waves per SIMD
+    __shared__ __attribute__((aligned(1024))) char kb0[UNIT_B];
+    __shared__ __attribute__((aligned(1024))) char kb1[UNIT_B];
 
-    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int q = lane & 31, hk = lane >> 5;
 
     // Decode: block-row groups in descending order (long rows first).
@@ -406,7 +425,6 @@ __global__ __launch_bounds__(256, 2) void rr_score32(const uint16_t *__restrict_
     const int NT = (rows_here + 31) >> 5;
     const int Itop = min(I0 + R, nb) - 1;
     const size_t plane = (size_t)Hkv * ns * D;
-    const uint16_t *kb = Kp + (size_t)g * ns * D;
 
     // Row f (0..rows_here) -> (block-row, head, stride); -1 stride if invalid.
     auto row_of = [&](int f, int &I, int &h, int &i) {
@@ -418,155 +436,165 @@ __global__ __launch_bounds__(256, 2) void rr_score32(const uint16_t *__restrict_
         i = (f < rows_here && a < cI) ? I * C + a : -1;
     };
 
-    // Stage the Q rows in LDS: chunk c of row f at slot c ^ (f & 15).
-    for (int idx = threadIdx.x; idx < kScoreRows * CPR; idx += 256) {
-        const int f = idx / CPR, c = idx % CPR;
+    // This wave's two row tiles: lane row, head and Q fragments (B operand:
+    // lane (q, half) holds d = 16 ks + 8 half .. + 7 of row q).
+    const int nt_w = min(max(NT - 2 * wid, 0), 2);   // valid tiles of this wave (wave-uniform)
+    int row_i[2], row_h[2];
+    bf16x8 qf[2][NKS];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
         int I, h, i;
-        row_of(f, I, h, i);
-        uint4 v = zero_u4();
-        if (i >= 0) {
-            const int t = i * S + (h % S);
-            v = ld16(Q + ((size_t)t * Hq + h) * D + c * 8);
+        row_of((2 * wid + u) * 32 + q, I, h, i);
+        row_i[u] = (u < nt_w) ? i : -1;
+        row_h[u] = h;
+        const uint16_t *qp = Q + ((size_t)(max(i, 0) * S + (h % S)) * Hq + h) * D + hk * 8;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            qf[u][ks] = as_bf16x8(row_i[u] >= 0 ? ld16(qp + ks * 16) : zero_u4());
+    }
+    // Last stride any row of this wave scores (units past it are skipped).
+    int imax = max(row_i[0], row_i[1]);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) imax = max(imax, __shfl_xor(imax, o, 64));
+    imax = __builtin_amdgcn_readfirstlane(imax);
+
+    float rM[2] = {-INFINITY, -INFINITY}, rZ[2] = {0.f, 0.f};
+
+    // Copies: copy c of this wave moves 64 16-byte chunks of plane c / CPP;
+    // LDS slot (row r, s) holds source chunk s ^ swz(r).
+    uint32_t coff[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const int p = ((wid * CPW + c) % CPP) * 64 + lane;
+        const int r = p / CPR, s = p % CPR;
+        coff[c] = (uint32_t)((r * D + (s ^ score_swz<D>(r)) * 8) * 2);
+    }
+    const uint16_t *kbase = Kp + (size_t)g * ns * D;
+    auto issue = [&](int t, char *kb) {
+        const int j0 = t * 32;
+        const int bytes = max(ns - j0, 0) * D * 2;
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const int cc = wid * CPW + c;
+            const __amdgpu_buffer_rsrc_t r =
+                buf_rsrc_n(kbase + (cc / CPP) * plane + (size_t)j0 * D, bytes);
+            buf2lds16(r, coff[c], (lds_char *)kb + cc * 1024);
         }
-        st16(&qs[f * D + ((c ^ (f & 15)) & (CPR - 1)) * 8], v);
-    }
+    };
 
-    // This lane's row in each tile.
-    int row_i[MT], row_h[MT];
-#pragma unroll
-    for (int rt = 0; rt < MT; ++rt) {
-        int I, h, i;
-        row_of(rt * 32 + q, I, h, i);
-        row_i[rt] = (rt < NT) ? i : -1;
-        row_h[rt] = h;
-    }
-    __syncthreads();
-
-    float rM[MT], rZ[MT];
-#pragma unroll
-    for (int rt = 0; rt < MT; ++rt) {
-        rM[rt] = -INFINITY;
-        rZ[rt] = 0.f;
-    }
-
-    // 32-stride units over the strides of blocks 0..Itop.
-    const int nu = ((Itop + 1) * C + 31) / 32;
-    const int nunits = (nu > wid) ? (nu - 1 - wid) / 4 + 1 : 0;
     // Pooled-key row of this lane's A operand (see the permutation above).
     const int krow = 16 * ((q >> 2) & 1) + 4 * (q >> 3) + (q & 3);
-    bf16x8 ka[3][NKS];
-    auto load_step = [&](int t, int ks) {
-        const int jr = min((wid + 4 * t) * 32 + krow, ns - 1);
-        const uint16_t *src = kb + (size_t)jr * D + ks * 16 + hk * 8;
-#pragma unroll
-        for (int p = 0; p < 3; ++p) ka[p][ks] = as_bf16x8(ld16(src + p * plane));
-    };
-    if (nunits > 0) {
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) load_step(0, ks);
-    }
+    const int ksw = score_swz<D>(krow);
 
-    // Q fragment ks of row tile rt (rows rt*32 + q: slot swizzle q & 15).
-    auto rdq = [&](int rt, int ks) {
-        const int c = 2 * ks + hk;
-        return as_bf16x8(ld16(&qs[(rt * 32 + q) * D + ((c ^ (q & 15)) & (CPR - 1)) * 8]));
+    // Block statistics of one tile's 32 x 32 scores for unit j0.
+    auto tile_stats = [&](int u, f32x16 &acc, int j0, bool diag) {
+        const int ri = row_i[u];
+        if (diag) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (j0 + 16 * hk + e > ri) acc[e] = -INFINITY;
+        }
+#pragma unroll
+        for (int bi = 0; bi < BPL; ++bi) {
+            float mr = -INFINITY;
+#pragma unroll
+            for (int e = bi * C; e < (bi + 1) * C; ++e) mr = fmaxf(mr, acc[e]);
+            const float m = mr * scale2;
+            const float mu = (mr == -INFINITY) ? 0.f : m;
+            // The block's C exponentials summed as two interleaved chains.
+            float z0 = fast_exp2(fmaf(acc[bi * C], scale2, -mu));
+            float z1 = fast_exp2(fmaf(acc[bi * C + 1], scale2, -mu));
+#pragma unroll
+            for (int e = 2; e < C; e += 2) {
+                z0 += fast_exp2(fmaf(acc[bi * C + e], scale2, -mu));
+                z1 += fast_exp2(fmaf(acc[bi * C + e + 1], scale2, -mu));
+            }
+            const float z = z0 + z1;
+            // A block with an unmasked stride j <= i lies at or before the
+            // row's own block.
+            const bool ok = ri >= 0 && mr != -INFINITY;
+            if (ok) {
+                const int J = (j0 + 16 * hk) / C + bi;
+                const int I = ri / C, a = ri - I * C;
+                stats[(size_t)row_h[u] * P + packed_offset(C, I, a, J)] = make_float2(m, z);
+            }
+            // Exact online merge into the row total with one exponential:
+            // e = 2^-|m - rM| scales whichever side is smaller.
+            const float dd = m - rM[u];
+            const float e = fast_exp2(-fabsf(dd));
+            const float nz = dd > 0.f ? fmaf(rZ[u], e, z) : fmaf(z, e, rZ[u]);
+            rZ[u] = ok ? nz : rZ[u];
+            rM[u] = ok ? fmaxf(rM[u], m) : rM[u];
+        }
     };
-    bf16x8 qn[2] = {rdq(0, 0), rdq(0, 1)};
 
-    for (int t = 0; t < nunits; ++t) {
-        const int j0 = (wid + 4 * t) * 32;
-        const bool refill = t + 1 < nunits;
+    // Products and statistics of unit t (pooled keys in kb) for NTW tiles.
+    auto compute = [&](auto ntw, int t, const char *kb) {
+        constexpr int NTW = decltype(ntw)::value;
+        const int j0 = t * 32;
+        const char *kr = kb + krow * (D * 2);
+        uint4 fr[NKS][3];
+        auto rd = [&](int ks) {
+            const int off = ((2 * ks + hk) ^ ksw) << 4;
+#pragma unroll
+            for (int p = 0; p < 3; ++p) fr[ks][p] = *reinterpret_cast<const uint4 *>(kr + p * PLANE_B + off);
+        };
+        f32x16 acc[NTW];
+#pragma unroll
+        for (int u = 0; u < NTW; ++u)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[u][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < LA; ++ks) rd(ks);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            if (ks + LA < NKS) rd(ks + LA);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+#pragma unroll
+                for (int u = 0; u < NTW; ++u) acc[u] = mfma32x32x16(as_bf16x8(fr[ks][p]), qf[u][ks], acc[u]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // Causal masking only where the unit reaches the first stride of block I0.
         const bool diag = j0 + 31 >= I0 * C;
 #pragma unroll
-        for (int rt = 0; rt < MT; ++rt) {
-            if (rt >= NT) break;
-            const bool last = rt == NT - 1;
-            f32x16 acc;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-            // Q fragments are read from LDS two steps ahead of their products;
-            // the last two steps read the next tile's first two (tile 0 again
-            // after the last tile: the rows stay for every unit).
-            const int rt_next = last ? 0 : rt + 1;
-            bf16x8 qf[NKS];
-            qf[0] = qn[0];
-            qf[1] = qn[1];
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                if (ks + 2 < NKS)
-                    qf[ks + 2] = rdq(rt, ks + 2);
-                else
-                    qn[ks + 2 - NKS] = rdq(rt_next, ks + 2 - NKS);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int p = 0; p < 3; ++p) acc = mfma32x32x16(ka[p][ks], qf[ks], acc);
-                if (last && refill) load_step(t + 1, ks);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            const int ri = row_i[rt];
-            if (diag) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    if (j0 + 16 * hk + e > ri) acc[e] = -INFINITY;
-            }
-#pragma unroll
-            for (int bi = 0; bi < BPL; ++bi) {
-                float mr = -INFINITY;
-#pragma unroll
-                for (int e = bi * C; e < (bi + 1) * C; ++e) mr = fmaxf(mr, acc[e]);
-                const float m = mr * scale2;
-                const float mu = (mr == -INFINITY) ? 0.f : m;
-                // The block's C exponentials summed as two interleaved chains.
-                float z0 = fast_exp2(fmaf(acc[bi * C], scale2, -mu));
-                float z1 = fast_exp2(fmaf(acc[bi * C + 1], scale2, -mu));
-#pragma unroll
-                for (int e = 2; e < C; e += 2) {
-                    z0 += fast_exp2(fmaf(acc[bi * C + e], scale2, -mu));
-                    z1 += fast_exp2(fmaf(acc[bi * C + e + 1], scale2, -mu));
-                }
-                const float z = z0 + z1;
-                // A block with an unmasked stride j <= i lies at or before the
-                // row's own block.
-                const bool ok = ri >= 0 && mr != -INFINITY;
-                if (ok) {
-                    const int J = (j0 + 16 * hk) / C + bi;
-                    const int I = ri / C, a = ri - I * C;
-                    stats[(size_t)row_h[rt] * P + packed_offset(C, I, a, J)] = make_float2(m, z);
-                }
-                // Exact online merge into the row total with one exponential:
-                // e = 2^-|m - rM| scales whichever side is smaller.
-                {
-                    const float dd = m - rM[rt];
-                    const float e = fast_exp2(-fabsf(dd));
-                    const float nz = dd > 0.f ? fmaf(rZ[rt], e, z) : fmaf(z, e, rZ[rt]);
-                    rZ[rt] = ok ? nz : rZ[rt];
-                    rM[rt] = ok ? fmaxf(rM[rt], m) : rM[rt];
-                }
-            }
-        }
-    }
+        for (int u = 0; u < NTW; ++u) tile_stats(u, acc[u], j0, diag);
+    };
+    auto unit = [&](int t, const char *kb) {
+        if (t * 32 > imax) return;     // every row of this wave ends before the unit
+        if (nt_w == 2)
+            compute(std::integral_constant<int, 2>(), t, kb);
+        else if (nt_w == 1)
+            compute(std::integral_constant<int, 1>(), t, kb);
+    };
 
-    // Per-row totals: the two lane halves hold other blocks of the same row;
-    // then across waves.
-#pragma unroll
-    for (int rt = 0; rt < MT; ++rt) {
-        const float m2 = xor_lane(rM[rt], 32), z2 = xor_lane(rZ[rt], 32);
-        merge_max_sum(rM[rt], rZ[rt], m2, z2);
+    // Units over the strides of blocks 0..Itop, one barrier each: every
+    // wave's copies of unit t have landed (vmcnt 0) and every wave has read
+    // unit t-1's buffer (lgkmcnt 0) before the copies of unit t+1 start.
+    const int nu = ((Itop + 1) * C + 31) / 32;
+    issue(0, kb0);
+    for (int t = 0; t < nu; t += 2) {
+        wait_vmcnt<0>();
+        wait_lgkm0();
+        bar();
+        if (t + 1 < nu) issue(t + 1, kb1);
+        unit(t, kb0);
+        if (t + 1 >= nu) break;
+        wait_vmcnt<0>();
+        wait_lgkm0();
+        bar();
+        if (t + 2 < nu) issue(t + 2, kb0);
+        unit(t + 1, kb1);
     }
-    if (hk == 0) {
+    wait_vmcnt<0>();
+
+    // Per-row totals: the two lane halves hold other blocks of the same row.
 #pragma unroll
-        for (int rt = 0; rt < MT; ++rt) red[wid][rt * 32 + q] = make_float2(rM[rt], rZ[rt]);
-    }
-    __syncthreads();
-    {
-        const int r = threadIdx.x;  // kScoreRows == 256 threads
-        float M = -INFINITY, Z = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) merge_max_sum(M, Z, red[w][r].x, red[w][r].y);
-        int I, h, i;
-        row_of(r, I, h, i);
-        if (i >= 0) rowstat[(size_t)h * ns + i] = make_float2(M, Z);
+    for (int u = 0; u < 2; ++u) {
+        const float m2 = xor_lane(rM[u], 32), z2 = xor_lane(rZ[u], 32);
+        merge_max_sum(rM[u], rZ[u], m2, z2);
+        if (hk == 0 && row_i[u] >= 0) rowstat[(size_t)row_h[u] * ns + row_i[u]] = make_float2(rM[u], rZ[u]);
     }
 }
 
@@ -574,11 +602,13 @@ __global__ __launch_bounds__(256, 2) void rr_score32(const uint16_t *__restrict_
 // rr_stride_softmax_pool: one work-group per (block-row I, query head h).
 // A[h][I][J] = sum_a z(a,J) 2^(m(a,J) - M_a) / Z_a over the strides a of
 // block I, i.e. the causal softmax of each sampled row summed over the
-// block's strides.  Thread p of a pass reads packed entry p (J = p / C,
-// a = p % C), so the block-row's entries are read once, coalesced; the C
-// terms of one J are summed by a fixed butterfly over lanes (and, for
-// C = 128, over the two waves holding the halves), so the result does not
-// depend on timing.  Entries J > I are written as zero.
+// block's strides.  For C >= 2, lane t of a pass reads the entry pair
+// 2t, 2t+1 (one 16-byte load; a pair never straddles two key blocks), adds
+// its two terms and the C/2 lanes of one J are summed by a fixed butterfly;
+// each thread keeps four loads in flight.  For C = 1 thread p reads entry
+// p.  The block-row's entries are read once, coalesced, and every sum runs
+// in a fixed order, so the result does not depend on timing.  Entries J > I
+// are written as zero.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void rr_stride_softmax_pool(const float2 *__restrict__ stats,
                                                               const float2 *__restrict__ rowstat,
@@ -587,7 +617,6 @@ __global__ __launch_bounds__(256) void rr_stride_softmax_pool(const float2 *__re
     const int I = blockIdx.x, h = blockIdx.y;
     const int cI = min(C, ns - I * C);
     __shared__ float sM[128], sInvZ[128];
-    __shared__ float part[4];
     for (int a = threadIdx.x; a < cI; a += blockDim.x) {
         float2 rs = rowstat[(size_t)h * ns + I * C + a];
         sM[a] = rs.x;
@@ -598,27 +627,39 @@ __global__ __launch_bounds__(256) void rr_stride_softmax_pool(const float2 *__re
     float *out = A + ((size_t)h * nb + I) * nb;
     const int span = (I + 1) * C;
     const int lg2C = __builtin_ctz(C);
-    const int group = C < kWave ? C : kWave;  // lanes summed by the butterfly
-    for (int p0 = 0; p0 < span; p0 += 256) {
-        const int p = p0 + (int)threadIdx.x;
-        const int J = p >> lg2C, a = p & (C - 1);
-        float v = 0.f;
-        if (p < span && a < cI) {
-            const float2 st = base[p];
-            v = st.y * fast_exp2(st.x - sM[a]) * sInvZ[a];
-        }
-        for (int o = 1; o < group; o <<= 1) v += xor_lane(v, o);
-        if (C <= kWave) {
-            if (p < span && (a & (group - 1)) == 0) out[J] = v;
-        } else {
-            // C == 128: waves 2k and 2k+1 hold the two halves of one J.
-            if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = v;
-            __syncthreads();
-            if (threadIdx.x < 2) {
-                const int Jo = (p0 >> lg2C) + (int)threadIdx.x;
-                if (Jo <= I) out[Jo] = part[2 * threadIdx.x] + part[2 * threadIdx.x + 1];
+    if (C >= 2) {
+        // Entry pairs: the packed offsets C*I(I+1)/2 and h*P are even, so
+        // every pair is 16-byte aligned.
+        const float4 *b4 = reinterpret_cast<const float4 *>(base);
+        const int half = C >> 1;    // lanes holding one J
+        const int span2 = span >> 1;
+        for (int q0 = 0; q0 < span2; q0 += 4 * 256) {
+            float4 st[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int qq = q0 + u * 256 + (int)threadIdx.x;
+                st[u] = qq < span2 ? b4[qq] : make_float4(0.f, 0.f, 0.f, 0.f);
             }
-            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int qq = q0 + u * 256 + (int)threadIdx.x;
+                const int p = 2 * qq, J = p >> lg2C, a = p & (C - 1);
+                float v = 0.f;
+                if (qq < span2) {
+                    if (a < cI) v = st[u].y * fast_exp2(st[u].x - sM[a]) * sInvZ[a];
+                    if (a + 1 < cI) v += st[u].w * fast_exp2(st[u].z - sM[a + 1]) * sInvZ[a + 1];
+                }
+                for (int o = 1; o < half; o <<= 1) v += xor_lane(v, o);
+                if (qq < span2 && a == 0) out[J] = v;
+            }
+        }
+    } else {
+        for (int p0 = 0; p0 < span; p0 += 256) {
+            const int p = p0 + (int)threadIdx.x;
+            if (p < span) {
+                const float2 st = base[p];
+                out[p] = st.y * fast_exp2(st.x - sM[0]) * sInvZ[0];
+            }
         }
     }
     for (int J = I + 1 + (int)threadIdx.x; J < nb; J += blockDim.x) out[J] = 0.f;
