@@ -38,15 +38,16 @@ HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 CSRC = os.path.join(ROOT, "long_context_prefill_rr_amd", "csrc")
 # Committed rocprofv3 summaries, one per workload (its name in the file
 # name), each valid for the kernel sources listed (sha256 in the file).
-# A workload's figures sit either in per-kernel summaries (the 128K
-# workload) or in one summary of all its kernels (rr_prefill_kernels_*.md,
-# which names the attention and estimation source hashes separately).
+# A workload's figures sit in one summary of all its kernels
+# (rr_prefill_kernels_<workload>.md), which names the attention and the
+# estimation source hashes separately; a per-kernel summary with a single
+# source_sha256 is read the same way.
 _ATTN_SRC = ["rr_attn.hip", "rr_device.h"]
 _EST_SRC = ["rr_estimate.hip", "rr_select.hip"]
-ATTN_TRAFFIC = (["rr_block_sparse_fa_{}_traffic.md", "rr_prefill_kernels_{}.md"], _ATTN_SRC, "attn")
-EST_TRAFFIC = (["rr_estimate_select_{}_traffic.md", "rr_prefill_kernels_{}.md"], _EST_SRC, "est")
-MFMA_BUSY = (["rr_block_sparse_fa_{}_mfma_busy.md", "rr_prefill_kernels_{}.md"], _ATTN_SRC, "attn")
-MAT_TRAFFIC = (["rr_estimate_materialized_{}_traffic.md", "rr_prefill_kernels_{}.md"], _EST_SRC, "est",
+ATTN_TRAFFIC = (["rr_prefill_kernels_{}.md"], _ATTN_SRC, "attn")
+EST_TRAFFIC = (["rr_prefill_kernels_{}.md"], _EST_SRC, "est")
+MFMA_BUSY = (["rr_prefill_kernels_{}.md"], _ATTN_SRC, "attn")
+MAT_TRAFFIC = (["rr_prefill_kernels_{}.md"], _EST_SRC, "est",
                "materialized_")   # field prefix in the all-kernel summaries
 
 
