@@ -251,12 +251,20 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-    float m = -INFINITY, lsum = 0.f;
+    // Running reference maximum, kept negated (nm = -m) so the weights' FMA
+    // takes it as is; +inf until the first key is seen.
+    float nm = INFINITY, lsum = 0.f;
 
     // MFMA row r = col of the S^T tile reads K row 16*((r>>2)&1) + 4*(r>>3) + (r&3)
     // of its 32-key sub-tile, so accumulator e of lane (col, hk) is key 16*hk + e.
     const int krow = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
     const int ksw = swz_k<D>(krow);
+    // Byte offset of this lane's K fragment of d-step ks inside a stage buffer
+    // (row krow, swizzled slot): the buffer's own address is then a constant
+    // that the LDS read takes in its offset field.
+    uint32_t kfo[C::NKS];
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) kfo[ks] = (uint32_t)(krow * (D * 2) + (((2 * ks + hk) ^ ksw) << 4));
     const int vsw = swz_v(col);
 
     const int nst = nunion * C::SPB;
@@ -326,13 +334,10 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
-        const char *kr0 = kb + krow * (D * 2);
-        const char *kr1 = kr0 + 32 * (D * 2);
         uint4 fa[C::NKS], fb[C::NKS];
         auto rd = [&](int ks) {
-            const int off = ((2 * ks + hk) ^ ksw) << 4;
-            fa[ks] = *reinterpret_cast<const uint4 *>(kr0 + off);
-            fb[ks] = *reinterpret_cast<const uint4 *>(kr1 + off);
+            fa[ks] = *reinterpret_cast<const uint4 *>(kb + kfo[ks]);
+            fb[ks] = *reinterpret_cast<const uint4 *>(kb + kfo[ks] + 32 * (D * 2));
         };
 #pragma unroll
         for (int ks = 0; ks < KLA; ++ks) rd(ks);
@@ -385,22 +390,22 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
                     gsum = add_bf16x2(pk[e], gsum);
                 }
             };
-            weights(-m);
+            weights(nm);
             if (__ballot(!(gsum <= kGroupMax)) != 0ull) {
                 // Maximum over the group (both lane halves hold the same
                 // query row).
                 float mx = -INFINITY;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sacc[kt][8 * mm + e]);
-                const float mn = fmaxf(m, max_halves(mx) * scale2);
-                const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
-                m = mn;
+                const float mn = fmaxf(-nm, max_halves(mx) * scale2);
+                const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(-nm - mn);
+                nm = -mn;
                 lsum *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-                weights(-m);
+                weights(nm);
             }
             lsum += gsum;
             const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
