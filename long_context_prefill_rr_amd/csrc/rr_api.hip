@@ -68,6 +68,20 @@ int run_attn(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const Shap
 
 namespace rr {
 
+// Compute units of the current device (queried once per device).
+int device_cu_count() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 int check_prefill_args(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, int Hq,
                        int Hkv, int d, int B, int S, float tau, const void *O, int o_dtype,
                        const int32_t *counts, const int32_t *block_idx) {

@@ -492,19 +492,6 @@ constexpr int kPersistMaxNb = 512;
 // faster at 8K (4 items per CU).
 constexpr int kInterleaveMaxItemsPerCu = 8;
 
-// Compute units of the current device (queried once per device).
-static int device_cu_count() {
-    static int cached[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] <= 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
 
 template <int D, int BLK>
 static void launch_fa_t(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, unsigned *counter,

@@ -372,7 +372,7 @@ __global__ __launch_bounds__(256) void rr_score(const uint16_t *__restrict__ Q,
 // rr_score spread a block over four lanes).
 //
 // The four waves walk the 32-stride units 0, 1, ... together, and wave w
-// owns row tiles 2w and 2w+1 for the whole pass: their Q fragments stay in
+// owns row tiles w and w+4 for the whole pass: their Q fragments stay in
 // registers, and every pooled-key fragment read from LDS feeds the products
 // of both tiles (two independent accumulation chains).  Each unit's three
 // planes (32 strides x d) are copied global -> LDS by the work-group
@@ -436,15 +436,16 @@ __global__ __launch_bounds__(256, 3) void rr_score32(const uint16_t *__restrict_
         i = (f < rows_here && a < cI) ? I * C + a : -1;
     };
 
-    // This wave's two row tiles: lane row, head and Q fragments (B operand:
-    // lane (q, half) holds d = 16 ks + 8 half .. + 7 of row q).
-    const int nt_w = min(max(NT - 2 * wid, 0), 2);   // valid tiles of this wave (wave-uniform)
+    // This wave's row tiles w and w+4 (so a 4-tile work-group keeps every
+    // wave busy): lane row, head and Q fragments (B operand: lane (q, half)
+    // holds d = 16 ks + 8 half .. + 7 of row q).
+    const int nt_w = (wid < NT ? 1 : 0) + (wid + 4 < NT ? 1 : 0);   // valid tiles (wave-uniform)
     int row_i[2], row_h[2];
     bf16x8 qf[2][NKS];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         int I, h, i;
-        row_of((2 * wid + u) * 32 + q, I, h, i);
+        row_of((wid + 4 * u) * 32 + q, I, h, i);
         row_i[u] = (u < nt_w) ? i : -1;
         row_h[u] = h;
         const uint16_t *qp = Q + ((size_t)(max(i, 0) * S + (h % S)) * Hq + h) * D + hk * 8;
@@ -762,7 +763,13 @@ hipError_t launch_pool_k(const uint16_t *K, const Shape &s, uint16_t *kplanes, h
 template <int D>
 static void launch_score_d(const uint16_t *Q, const Shape &s, const EstimateWs &w, hipStream_t st) {
     const int GC = s.G * s.c;
-    const int R = std::max(1, std::min(s.nb, kScoreRows / GC));  // block-rows per work-group
+    int R = std::max(1, std::min(s.nb, kScoreRows / GC));  // block-rows per work-group
+    if (s.c == 4 || s.c == 8 || s.c == 16) {
+        // Short inputs: fewer block-rows per work-group (down to four 32-row
+        // tiles, one per wave) until there are about two work-groups per CU.
+        const int want = 2 * device_cu_count();
+        while (R > 1 && (R / 2) * GC >= 128 && ((s.nb + R - 1) / R) * s.Hkv < want) R /= 2;
+    }
     const int nchunks = (R * GC + kScoreRows - 1) / kScoreRows;
     const int ngrp = (s.nb + R - 1) / R;
     const dim3 grid((unsigned)(ngrp * s.Hkv * nchunks));

@@ -79,6 +79,9 @@ int run_prefill(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, 
                 int d, int B, int S, float tau, void *O, int o_dtype, int32_t *counts,
                 int32_t *block_idx, void *ws, void *stream);
 
+// Compute units of the current device (queried once per device).
+int device_cu_count();
+
 // Launchers (enqueue on `stream`, return the launch error).
 hipError_t launch_pool_k(const uint16_t *K, const Shape &s, uint16_t *kplanes, hipStream_t st);
 hipError_t launch_score(const uint16_t *Q, const Shape &s, const EstimateWs &w, hipStream_t st);
