@@ -37,11 +37,19 @@
 // block-row descending within one kv-head at a time (all kv-heads together
 // when each CU takes at most 8 items), then kv-head and head pair: long rows
 // start first, the K/V in use stays in the last-level cache, and a CU that
-// finishes an item early simply takes the next.  Up to 512 blocks the
-// work-groups are persistent (one per CU, looping over items), so none is
-// launched or torn down between the short items.  (Work-groups are dealt to
+// finishes an item early simply takes the next.  (Work-groups are dealt to
 // the 8 XCDs by block index; a fixed mapping from block index to rows left
 // the XCDs with up to 41% different work on the 64K video shape.)
+//
+// Up to 512 blocks (SINGLE) a work-group serves one query head: BLK/32 waves,
+// two stage buffers with one barrier per stage, and LDS for two work-groups
+// per CU.  The work-groups are persistent (two per CU, looping over items),
+// and the two waves a SIMD holds then belong to different work-groups whose
+// barriers are independent, so one wave's softmax meets the other's
+// products more often than in the head-pair work-group, whose barrier keeps
+// its two waves per SIMD in step; no wave waits on a stage its head did not
+// keep.  Longer rows keep the head pairs: there, sharing each staged K/V tile
+// between two heads matters more.
 #include <algorithm>
 
 #include "rr_device.h"
@@ -77,12 +85,13 @@ __global__ __launch_bounds__(256) void rr_transpose_v(const uint16_t *__restrict
 }
 
 // Tile constants of the attention kernel.  A work-group holds two head
-// groups of BLK/32 waves (two query heads that share one kv-head); each wave
-// owns one 32-row query tile.  Keys are walked in 64-key stages.
-template <int D, int BLK>
+// groups of BLK/32 waves (two query heads that share one kv-head), or one
+// with SINGLE; each wave owns one 32-row query tile.  Keys are walked in
+// 64-key stages.
+template <int D, int BLK, bool SINGLE = false>
 struct FaCfg {
     static constexpr int NWG = BLK / 32;                // waves per head group
-    static constexpr int NW = 2 * NWG;                  // waves per work-group
+    static constexpr int NW = SINGLE ? NWG : 2 * NWG;   // waves per work-group
     static constexpr int NT = NW * 64;                  // threads
     static constexpr int KT = 64;                       // keys per pipeline stage
     static constexpr int SPB = BLK / KT;                // stages per key block
@@ -94,7 +103,7 @@ struct FaCfg {
     static constexpr int VBYTES = D * KT * 2;
     static constexpr int NDT = D / 32;
     static constexpr int NKS = D / 16;
-    static constexpr int MAXNB = 4096;                  // longest block list
+    static constexpr int MAXNB = SINGLE ? 2048 : 4096;  // longest block list
 };
 
 // LDS swizzles (16-byte slot XOR per row) chosen so that the 16 rows read by
@@ -132,26 +141,27 @@ __device__ __forceinline__ float sum_halves(float x) {
 // A 64-row block makes a 4-wave work-group that fits once per CU (LDS): one
 // wave per SIMD.
 //
-// PERSIST: the grid holds about one work-group per CU and each loops over work
-// items; otherwise the grid holds one work-group per item (the loop body runs
-// once).  The loop costs registers, and at long rows (nb > 512) the launch of
-// a new work-group per item is a smaller cost than that.
-template <int D, int BLK, bool OUT_F32, bool PERSIST>
-__global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_fa(
+// PERSIST: the grid holds about one work-group per CU (two with SINGLE) and
+// each loops over work items; otherwise the grid holds one work-group per
+// item (the loop body runs once).  The loop costs registers, and at long rows
+// (nb > 512) the launch of a new work-group per item is a smaller cost than
+// that.  SINGLE: one query head per work-group (see the file header).
+template <int D, int BLK, bool OUT_F32, bool PERSIST, bool SINGLE>
+__global__ __launch_bounds__(SINGLE ? BLK * 2 : BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_fa(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ Vt,
     unsigned *__restrict__ counter, int nitems, int hchunk, int L, int Lp, int Hq, int Hkv, int nb,
     int nq,
     const int32_t *__restrict__ counts, const int32_t *__restrict__ block_idx, void *__restrict__ O,
     float scale2) {
-    using C = FaCfg<D, BLK>;
+    using C = FaCfg<D, BLK, SINGLE>;
     __shared__ __attribute__((aligned(1024))) char Kb0[C::KBYTES];
     __shared__ __attribute__((aligned(1024))) char Kb1[C::KBYTES];
-    __shared__ __attribute__((aligned(1024))) char Kb2[C::KBYTES];
-    __shared__ __attribute__((aligned(1024))) char Kb3[C::KBYTES];
+    __shared__ __attribute__((aligned(1024))) char Kb2[SINGLE ? 16 : C::KBYTES];
+    __shared__ __attribute__((aligned(1024))) char Kb3[SINGLE ? 16 : C::KBYTES];
     __shared__ __attribute__((aligned(1024))) char Vb0[C::VBYTES];
     __shared__ __attribute__((aligned(1024))) char Vb1[C::VBYTES];
-    __shared__ __attribute__((aligned(1024))) char Vb2[C::VBYTES];
-    __shared__ __attribute__((aligned(1024))) char Vb3[C::VBYTES];
+    __shared__ __attribute__((aligned(1024))) char Vb2[SINGLE ? 16 : C::VBYTES];
+    __shared__ __attribute__((aligned(1024))) char Vb3[SINGLE ? 16 : C::VBYTES];
     __shared__ uint32_t ulist[C::MAXNB];          // union of the two kept lists
     __shared__ uint32_t bits[2][C::MAXNB / 32];   // per-head membership bitmaps
     __shared__ int scan_part[C::NW];
@@ -180,14 +190,15 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(item_sh);
     if (item >= nitems) break;
-    const int per_chunk = hchunk * nb * npair;
+    const int nsub = SINGLE ? G : npair;      // items per (kv-head, block-row)
+    const int per_chunk = hchunk * nb * nsub;
     const int c_ = item / per_chunk, r_ = item - c_ * per_chunk;
-    const int I = nb - 1 - r_ / (hchunk * npair);
-    const int r2 = r_ % (hchunk * npair);
-    const int g = c_ * hchunk + r2 / npair;
-    const int pp = r2 % npair;
-    const bool head_ok = 2 * pp + gr < G;     // odd G: the last pair has one head
-    const int h = g * G + min(2 * pp + gr, G - 1);
+    const int I = nb - 1 - r_ / (hchunk * nsub);
+    const int r2 = r_ % (hchunk * nsub);
+    const int g = c_ * hchunk + r2 / nsub;
+    const int pp = r2 % nsub;                 // head pair, or the head itself with one head
+    const bool head_ok = SINGLE || 2 * pp + gr < G;     // odd G: the last pair has one head
+    const int h = SINGLE ? g * G + pp : g * G + min(2 * pp + gr, G - 1);
     const int tq = I * BLK + rw * 32 + col;
     const int wave_last_row = I * BLK + rw * 32 + 31;
 
@@ -199,8 +210,8 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        if (2 * pp + q >= G) continue;
-        const int hq = g * G + 2 * pp + q;
+        if (SINGLE ? q > 0 : 2 * pp + q >= G) continue;
+        const int hq = SINGLE ? g * G + pp : g * G + 2 * pp + q;
         const int cq = min(max(counts[(size_t)hq * nb + I], 0), nb);
         const int32_t *lq = block_idx + ((size_t)hq * nb + I) * nb;
         for (int k = tid; k < cq; k += C::NT) {
@@ -421,7 +432,32 @@ __global__ __launch_bounds__(BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_f
     // fill the other.  One barrier per pair: every wave's copies of the pair
     // have landed (vmcnt 0) and every wave has finished reading the other
     // pair (lgkmcnt 0) before it.
-    if (nst > 0) {
+    if constexpr (SINGLE) {
+        // One head: two buffers, one stage per barrier.
+        if (nst > 0) {
+            issue(0, Kb0, Vb0);
+            for (int st = 0; st < nst; st += 2) {
+                {
+                    const int E0 = stage_entry(st);
+                    wait_vmcnt<0>();
+                    wait_lgkm0();
+                    bar();
+                    issue(st + 1, Kb1, Vb1);
+                    compute(st, E0, Kb0, Vb0);
+                }
+                if (st + 1 >= nst) break;
+                {
+                    const int E1 = stage_entry(st + 1);
+                    wait_vmcnt<0>();
+                    wait_lgkm0();
+                    bar();
+                    issue(st + 2, Kb0, Vb0);
+                    compute(st + 1, E1, Kb1, Vb1);
+                }
+            }
+            wait_vmcnt<0>();
+        }
+    } else if (nst > 0) {
         issue(0, Kb0, Vb0);
         issue(1, Kb1, Vb1);
         for (int st = 0; st < nst; st += 4) {
@@ -493,38 +529,36 @@ constexpr int kPersistMaxNb = 512;
 constexpr int kInterleaveMaxItemsPerCu = 8;
 
 
-template <int D, int BLK>
+template <int D, int BLK, bool SINGLE>
 static void launch_fa_t(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, unsigned *counter,
                         const Shape &s, const int32_t *counts, const int32_t *block_idx, void *O,
                         bool out_f32, hipStream_t st) {
+    using C = FaCfg<D, BLK, SINGLE>;
     const int nq = s.nb * s.Hkv;
-    const int nitems = nq * ((s.G + 1) / 2);
-    // kv-heads per chunk of the item order: all of them for few items per
-    // CU, else one.
+    const int nitems = nq * (SINGLE ? s.G : (s.G + 1) / 2);
     const int ncu = device_cu_count();
-    const int hchunk = nitems <= kInterleaveMaxItemsPerCu * ncu ? s.Hkv : 1;
+    const int hchunk = nitems <= kInterleaveMaxItemsPerCu * (SINGLE ? 2 : 1) * ncu ? s.Hkv : 1;
     const float scale2 = kLog2e / sqrtf((float)D);
     const int Lp = s.nb * BLK;
-    const dim3 block(BLK * 4);
+    const dim3 block(C::NT);
     if (s.nb <= kPersistMaxNb) {
-        // One persistent work-group per CU (each holds most of a CU's LDS).
-        const dim3 grid((unsigned)std::min(nitems, ncu));
+        const dim3 grid((unsigned)std::min(nitems, (SINGLE ? 2 : 1) * ncu));
         if (out_f32)
-            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true, true>), grid, block, 0, st, Q, K, Vt,
+            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true, true, SINGLE>), grid, block, 0, st, Q, K, Vt,
                                counter, nitems, hchunk, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O,
                                scale2);
         else
-            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false, true>), grid, block, 0, st, Q, K, Vt,
+            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false, true, SINGLE>), grid, block, 0, st, Q, K, Vt,
                                counter, nitems, hchunk, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O,
                                scale2);
     } else {
         const dim3 grid((unsigned)nitems);
         if (out_f32)
-            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true, false>), grid, block, 0, st, Q, K,
+            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true, false, SINGLE>), grid, block, 0, st, Q, K,
                                Vt, counter, nitems, hchunk, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts,
                                block_idx, O, scale2);
         else
-            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false, false>), grid, block, 0, st, Q, K,
+            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false, false, SINGLE>), grid, block, 0, st, Q, K,
                                Vt, counter, nitems, hchunk, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts,
                                block_idx, O, scale2);
     }
@@ -533,14 +567,19 @@ static void launch_fa_t(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt
 hipError_t launch_block_sparse_fa(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt,
                                   unsigned *counter, const Shape &s, const int32_t *counts,
                                   const int32_t *block_idx, void *O, bool out_f32, hipStream_t st) {
-    if (s.d == 128 && s.B == 128)
-        launch_fa_t<128, 128>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
-    else if (s.d == 128 && s.B == 64)
-        launch_fa_t<128, 64>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
-    else if (s.d == 64 && s.B == 128)
-        launch_fa_t<64, 128>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
-    else
-        launch_fa_t<64, 64>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
+    // Up to kPersistMaxNb blocks: one query head per work-group, two
+    // work-groups per CU (the persistent form); longer rows: head pairs.
+    const bool single = s.nb <= kPersistMaxNb;
+    if (s.d == 128 && s.B == 128) {
+        if (single) launch_fa_t<128, 128, true>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
+        else launch_fa_t<128, 128, false>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
+    } else if (s.d == 128 && s.B == 64)
+        launch_fa_t<128, 64, false>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
+    else if (s.d == 64 && s.B == 128) {
+        if (single) launch_fa_t<64, 128, true>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
+        else launch_fa_t<64, 128, false>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
+    } else
+        launch_fa_t<64, 64, false>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
     return hipGetLastError();
 }
 
