@@ -529,38 +529,49 @@ constexpr int kPersistMaxNb = 512;
 constexpr int kInterleaveMaxItemsPerCu = 8;
 
 
+template <int D, int BLK, bool OUT_F32, bool PERSIST, bool SINGLE>
+static void launch_fa_k(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, unsigned *counter,
+                        const Shape &s, int nitems, int hchunk, const int32_t *counts,
+                        const int32_t *block_idx, void *O, unsigned grid, hipStream_t st) {
+    const float scale2 = kLog2e / sqrtf((float)D);
+    hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, OUT_F32, PERSIST, SINGLE>), dim3(grid),
+                       dim3(FaCfg<D, BLK, SINGLE>::NT), 0, st, Q, K, Vt, counter, nitems, hchunk, s.L,
+                       s.nb * BLK, s.Hq, s.Hkv, s.nb, s.nb * s.Hkv, counts, block_idx, O, scale2);
+}
+
+// SINGLE (one head per work-group) is launched in the persistent form only,
+// as are head pairs of 64-row blocks up to kPersistMaxNb blocks; head pairs of
+// 128-row blocks serve rows longer than that, one work-group per item.
 template <int D, int BLK, bool SINGLE>
 static void launch_fa_t(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, unsigned *counter,
                         const Shape &s, const int32_t *counts, const int32_t *block_idx, void *O,
                         bool out_f32, hipStream_t st) {
-    using C = FaCfg<D, BLK, SINGLE>;
-    const int nq = s.nb * s.Hkv;
-    const int nitems = nq * (SINGLE ? s.G : (s.G + 1) / 2);
+    const int nitems = s.nb * s.Hkv * (SINGLE ? s.G : (s.G + 1) / 2);
     const int ncu = device_cu_count();
-    const int hchunk = nitems <= kInterleaveMaxItemsPerCu * (SINGLE ? 2 : 1) * ncu ? s.Hkv : 1;
-    const float scale2 = kLog2e / sqrtf((float)D);
-    const int Lp = s.nb * BLK;
-    const dim3 block(C::NT);
-    if (s.nb <= kPersistMaxNb) {
-        const dim3 grid((unsigned)std::min(nitems, (SINGLE ? 2 : 1) * ncu));
-        if (out_f32)
-            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true, true, SINGLE>), grid, block, 0, st, Q, K, Vt,
-                               counter, nitems, hchunk, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O,
-                               scale2);
-        else
-            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false, true, SINGLE>), grid, block, 0, st, Q, K, Vt,
-                               counter, nitems, hchunk, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts, block_idx, O,
-                               scale2);
+    const int slots = (SINGLE ? 2 : 1) * ncu;   // resident work-groups of the persistent form
+    const int hchunk = nitems <= kInterleaveMaxItemsPerCu * slots ? s.Hkv : 1;
+    constexpr bool kPersistOnly = SINGLE;
+    constexpr bool kPersistNever = !SINGLE && BLK == 128;
+    const bool persist = kPersistOnly || (!kPersistNever && s.nb <= kPersistMaxNb);
+    if (persist) {
+        if constexpr (!kPersistNever) {
+            const unsigned grid = (unsigned)std::min(nitems, slots);
+            if (out_f32)
+                launch_fa_k<D, BLK, true, true, SINGLE>(Q, K, Vt, counter, s, nitems, hchunk, counts, block_idx, O,
+                                                        grid, st);
+            else
+                launch_fa_k<D, BLK, false, true, SINGLE>(Q, K, Vt, counter, s, nitems, hchunk, counts, block_idx,
+                                                         O, grid, st);
+        }
     } else {
-        const dim3 grid((unsigned)nitems);
-        if (out_f32)
-            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, true, false, SINGLE>), grid, block, 0, st, Q, K,
-                               Vt, counter, nitems, hchunk, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts,
-                               block_idx, O, scale2);
-        else
-            hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, false, false, SINGLE>), grid, block, 0, st, Q, K,
-                               Vt, counter, nitems, hchunk, s.L, Lp, s.Hq, s.Hkv, s.nb, nq, counts,
-                               block_idx, O, scale2);
+        if constexpr (!kPersistOnly) {
+            if (out_f32)
+                launch_fa_k<D, BLK, true, false, SINGLE>(Q, K, Vt, counter, s, nitems, hchunk, counts, block_idx,
+                                                         O, (unsigned)nitems, st);
+            else
+                launch_fa_k<D, BLK, false, false, SINGLE>(Q, K, Vt, counter, s, nitems, hchunk, counts,
+                                                          block_idx, O, (unsigned)nitems, st);
+        }
     }
 }
 
