@@ -12,7 +12,9 @@ the largest supported block count.
   levels, so most cuts fall inside a run of ties: every sum is exact in
   fp32 and fp64 alike, so the lists must equal the oracle's exactly;
 * nb = 4096 (L = 524288 at B = 128), the largest list the selection takes:
-  end to end, checked on sampled block-rows and tokens.
+  end to end, checked on sampled block-rows and tokens;
+* attention on rows of more than 512 blocks (head-pair work-groups) with an
+  odd G and with 64-row blocks, on random causal masks.
 Rules as for the other parity tests: masks equal up to blocks within 1e-4 of
 the tau boundary, block scores to 1e-5 of the row total, attention outputs
 max |err| <= 1e-2 and mean <= 1e-3 (fp32 output).
@@ -187,6 +189,48 @@ def test_largest_block_count():
     for h, I in rows:
         lo = I * B
         toks += [(h, lo), (h, lo + 63), (h, lo + B - 1)]
+    O_ref = oracle.attention(g["q"], g["k"], g["v"], B, mask, toks=toks)
+    O_np = O.cpu().numpy()
+    got = np.stack([O_np[t, h] for h, t in toks])
+    mx, mean = o_errors(got, O_ref)
+    print("  O on %d tokens: max %.3g mean %.3g" % (len(toks), mx, mean), flush=True)
+    assert mx <= O_MAX and mean <= O_MEAN
+
+
+# Rows of more than 512 blocks take the head-pair work-groups (shorter rows
+# take one head per work-group): an odd G, whose last pair has a single head,
+# and 64-row blocks, both on random causal masks.  Whole block-rows of every
+# head are compared with the oracle.
+LONG_ROWS = [
+    # (L, Hq, Hkv, d, B)
+    (520 * 128 - 37, 3, 1, 64, 128),   # G = 3: pairs (0, 1) and (2, -); ragged last block
+    (520 * 64 - 5, 2, 1, 128, 64),     # 64-row blocks, one pair
+]
+
+
+@pytest.mark.parametrize("case", LONG_ROWS, ids=[str(c) for c in LONG_ROWS])
+def test_long_rows_head_pair_forms(case):
+    rr = _rr()
+    L, Hq, Hkv, d, B = case
+    w, g = small_workload(kind="llama", L=L, Hq=Hq, Hkv=Hkv, d=d, B=B, S=8, seed=29)
+    nb = w.nb
+    assert nb > 512
+    print("long rows %s nb=%d" % (case, nb), flush=True)
+    rng = np.random.default_rng(31)
+    mask = np.tril((rng.uniform(size=(Hq, nb, nb)) < 0.3).astype(np.uint8))
+    mask[:, np.arange(nb), np.arange(nb)] |= (rng.uniform(size=(Hq, nb)) < 0.5).astype(np.uint8)
+    for h in range(Hq):
+        for I in range(nb):
+            if not mask[h, I].any():
+                mask[h, I, rng.integers(0, I + 1)] = 1
+    counts, idx = oracle.list_from_mask(mask)
+    idx = np.where(np.arange(nb)[None, None, :] < counts[:, :, None], idx, -1).astype(np.int32)
+    q, k, v = _dev(g["q"]), _dev(g["k"]), _dev(g["v"])
+    O = rr.rr_sparse_attn(q, k, v, B, torch.from_numpy(counts).cuda(), torch.from_numpy(idx).cuda(),
+                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    toks = [(h, t) for h in range(Hq) for I in (0, 1, nb // 2, nb - 2, nb - 1)
+            for t in range(I * B, min((I + 1) * B, L))]
     O_ref = oracle.attention(g["q"], g["k"], g["v"], B, mask, toks=toks)
     O_np = O.cpu().numpy()
     got = np.stack([O_np[t, h] for h, t in toks])
