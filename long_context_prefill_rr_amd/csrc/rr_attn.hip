@@ -150,7 +150,6 @@ template <int D, int BLK, bool OUT_F32, bool PERSIST, bool SINGLE>
 __global__ __launch_bounds__(SINGLE ? BLK * 2 : BLK * 4, BLK == 128 ? 2 : 1) void rr_block_sparse_fa(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ Vt,
     unsigned *__restrict__ counter, int nitems, int hchunk, int L, int Lp, int Hq, int Hkv, int nb,
-    int nq,
     const int32_t *__restrict__ counts, const int32_t *__restrict__ block_idx, void *__restrict__ O,
     float scale2) {
     using C = FaCfg<D, BLK, SINGLE>;
@@ -203,9 +202,10 @@ __global__ __launch_bounds__(SINGLE ? BLK * 2 : BLK * 4, BLK == 128 ? 2 : 1) voi
     const int wave_last_row = I * BLK + rw * 32 + 31;
 
     // Union of the two heads' kept lists (ascending key blocks, each tagged
-    // with the heads that keep it), built in LDS: membership bitmaps, then a
-    // work-group scan compacts the set blocks in index order.
-    const int nbw = (nb + 31) >> 5;
+    // with the heads that keep it; with SINGLE the one head's list), built in
+    // LDS: membership bitmaps, then a work-group scan compacts the set blocks
+    // in index order.  The bitmaps also drop repeated and out-of-range
+    // entries of a malformed list.
     for (int i = tid; i < 2 * (C::MAXNB / 32); i += C::NT) (&bits[0][0])[i] = 0u;
     __syncthreads();
 #pragma unroll
@@ -248,7 +248,6 @@ __global__ __launch_bounds__(SINGLE ? BLK * 2 : BLK * 4, BLK == 128 ? 2 : 1) voi
         if (tid == C::NT - 1) nunion = pre + incl;
         __syncthreads();
     }
-    (void)nbw;
 
     bf16x8 qf[C::NKS];
     {
@@ -520,12 +519,13 @@ hipError_t launch_transpose_v(const uint16_t *V, const Shape &s, uint16_t *Vt, u
 
 // Longest block count for which the persistent form is launched.
 constexpr int kPersistMaxNb = 512;
-// Items per CU up to which the items of all kv-heads are interleaved
-// (block-rows descending over every kv-head: the longest rows start first,
-// which matters when each CU takes only a few items).  With more items per
-// CU one kv-head at a time keeps the K/V in use small: interleaving two
-// kv-heads measured 8% slower at 128K and 2.5% slower at 32K, all eight 10%
-// faster at 8K (4 items per CU).
+// Items per resident work-group (one per CU with head pairs, two with one
+// head) up to which the items of all kv-heads are interleaved (block-rows
+// descending over every kv-head: the longest rows start first, which matters
+// when each work-group takes only a few items).  With more items per
+// work-group one kv-head at a time keeps the K/V in use small: with head
+// pairs, interleaving two kv-heads measured 8% slower at 128K and 2.5%
+// slower at 32K, all eight 10% faster at 8K (4 items per CU).
 constexpr int kInterleaveMaxItemsPerCu = 8;
 
 
@@ -536,7 +536,7 @@ static void launch_fa_k(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt
     const float scale2 = kLog2e / sqrtf((float)D);
     hipLaunchKernelGGL((rr_block_sparse_fa<D, BLK, OUT_F32, PERSIST, SINGLE>), dim3(grid),
                        dim3(FaCfg<D, BLK, SINGLE>::NT), 0, st, Q, K, Vt, counter, nitems, hchunk, s.L,
-                       s.nb * BLK, s.Hq, s.Hkv, s.nb, s.nb * s.Hkv, counts, block_idx, O, scale2);
+                       s.nb * BLK, s.Hq, s.Hkv, s.nb, counts, block_idx, O, scale2);
 }
 
 // SINGLE (one head per work-group) is launched in the persistent form only,
