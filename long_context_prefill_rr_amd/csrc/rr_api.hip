@@ -5,6 +5,8 @@
 // the caller's stream.
 #include <math.h>
 
+#include <atomic>
+
 #include "rr.h"
 #include "rr_internal.h"
 
@@ -68,18 +70,19 @@ int run_attn(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const Shap
 
 namespace rr {
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; threads
+// that race on the first query store the same value).
 int device_cu_count() {
-    static int cached[64] = {};
+    static std::atomic<int> cached[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] <= 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 int check_prefill_args(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int L, int Hq,
