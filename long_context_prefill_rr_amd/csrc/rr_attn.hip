@@ -57,8 +57,8 @@
 
 namespace rr {
 
-// K fragments are read this many d-steps ahead of the products that use them.
-constexpr int KLA = 2;
+// K fragment reads kept in flight ahead of the products that use them.
+constexpr int KLA = 4;
 
 // V [L][Hkv][d] -> Vt [Hkv][d][Lp], tokens >= L zero-filled.  64x64 tiles.
 // Also resets the attention kernel's work counter.
@@ -115,15 +115,18 @@ __device__ __forceinline__ int swz_k(int r) {
 }
 __device__ __forceinline__ int swz_v(int r) { return (r >> 1) & 7; }
 
-// Online softmax with a checked reference maximum (log2 units).  A 16-key
-// group's weights are first formed against the running reference maximum m;
-// only if a lane's eight weights sum to more than kGroupMax (a score above m
-// by a few units, or m not yet set: an inf / NaN sum) is the group's maximum
-// taken, O and the normaliser rescaled, and the group's weights formed
-// again.  The common path computes no per-score maximum.  Weights stay <= 64,
-// and m follows the row maximum closely: the key that sets m gets weight
-// exactly 1, so the largest weights carry little bf16 rounding (a limit of
-// 4096 measured about 20% larger output errors).
+// Online softmax with a checked reference maximum (log2 units).  The weights
+// of a 32-key sub-tile (two 16-key groups) are first formed against the
+// running reference maximum m; only if a lane's eight weights of either group
+// sum to more than kGroupMax (a score above m by a few units, or m not yet
+// set: an inf / NaN sum) is the sub-tile's maximum taken, O and the
+// normaliser rescaled, and both groups' weights formed again.  The common
+// path computes no per-score maximum.  Weights stay <= 64, and m follows the
+// row maximum closely: the key that sets m gets weight exactly 1, so the
+// largest weights carry little bf16 rounding (a limit of 4096 measured about
+// 20% larger output errors).  The first sub-tile a row meets always holds an
+// unmasked key of that row (key 0 of its first kept block), so m is finite
+// before any fully masked group is weighed.
 constexpr float kGroupMax = 64.f;
 
 // max / sum of x over both 32-lane halves, for every lane (v_permlane32_swap).
@@ -335,78 +338,58 @@ __global__ __launch_bounds__(SINGLE ? BLK * 2 : BLK * 4, BLK == 128 ? 2 : 1) voi
         const bool diag = (J == I);
         if (diag && wave_last_row < key0) return;  // whole stage above this wave's rows
 
-        // S^T for both 32-key sub-tiles, d-step by d-step.  K fragments are
-        // read two d-steps ahead of their products; scheduling barriers keep
-        // the compiler from sinking each read next to its consumer, which
-        // would expose one LDS round trip per pair of products.
+        // S^T sub-tile 0 (keys key0 .. key0+31) first, then sub-tile 1, so
+        // that sub-tile 0's weights are formed while sub-tile 1's products
+        // run.  K fragments are read four steps ahead of their products.
         f32x16 sacc[2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
-        uint4 fa[C::NKS], fb[C::NKS];
-        auto rd = [&](int ks) {
-            fa[ks] = *reinterpret_cast<const uint4 *>(kb + kfo[ks]);
-            fb[ks] = *reinterpret_cast<const uint4 *>(kb + kfo[ks] + 32 * (D * 2));
+        constexpr int NS = 2 * C::NKS, LA = KLA;
+        uint4 kf[NS];
+        auto rd = [&](int s) {
+            kf[s] = *reinterpret_cast<const uint4 *>(kb + kfo[s % C::NKS] + (s / C::NKS) * 32 * (D * 2));
         };
-#pragma unroll
-        for (int ks = 0; ks < KLA; ++ks) rd(ks);
-#pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) {
-            if (ks + KLA < C::NKS) rd(ks + KLA);
-            __builtin_amdgcn_sched_barrier(0);
-            sacc[0] = mfma32x32x16(as_bf16x8(fa[ks]), qf[ks], sacc[0]);
-            sacc[1] = mfma32x32x16(as_bf16x8(fb[ks]), qf[ks], sacc[1]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-
         // V^T fragments of 16-key group gi (kt = gi / 2, mm = gi % 2), one per
-        // 32-row d-tile; groups 0 and 1 are read before the softmax starts and
-        // each later group's two groups ahead of its products.
+        // 32-row d-tile.
         auto rdv = [&](int gi, uint4 (&a)[C::NDT]) {
             const int voff = ((4 * (gi >> 1) + 2 * hk + (gi & 1)) ^ vsw) << 4;
 #pragma unroll
             for (int dt = 0; dt < C::NDT; ++dt)
                 a[dt] = *reinterpret_cast<const uint4 *>(vb + (dt * 32 + col) * (C::KT * 2) + voff);
         };
-        uint4 vf[4][C::NDT];
-        rdv(0, vf[0]);
-        rdv(1, vf[1]);
-        __builtin_amdgcn_sched_barrier(0);
-
-        if (diag) {
+        auto mask_diag = [&](int kt) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = key0 + kt * 32 + 16 * hk + e;
-                    if (key > tq) sacc[kt][e] = -INFINITY;
-                }
-        }
-
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
+            for (int e = 0; e < 16; ++e) {
+                const int key = key0 + kt * 32 + 16 * hk + e;
+                if (key > tq) sacc[kt][e] = -INFINITY;
+            }
+        };
+        // Weights of group gi against the reference maximum nm: packed bf16
+        // pairs and their sum (the normaliser sums the same bf16 weights the
+        // P.V product uses).
+        auto weights = [&](int gi, float nmv, uint32_t (&pk)[4]) -> float {
             const int kt = gi >> 1, mm = gi & 1;
-            uint32_t pk[4];
-            float gsum;
-            // The normaliser sums the same bf16 weights the P.V product uses.
-            auto weights = [&](float nm) {
-                gsum = 0.f;
+            float gs = 0.f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p0 = fast_exp2(fmaf(sacc[kt][8 * mm + 2 * e], scale2, nm));
-                    const float p1 = fast_exp2(fmaf(sacc[kt][8 * mm + 2 * e + 1], scale2, nm));
-                    pk[e] = pack_bf16x2(p0, p1);
-                    gsum = add_bf16x2(pk[e], gsum);
-                }
-            };
-            weights(nm);
-            if (__ballot(!(gsum <= kGroupMax)) != 0ull) {
-                // Maximum over the group (both lane halves hold the same
-                // query row).
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = fast_exp2(fmaf(sacc[kt][8 * mm + 2 * e], scale2, nmv));
+                const float p1 = fast_exp2(fmaf(sacc[kt][8 * mm + 2 * e + 1], scale2, nmv));
+                pk[e] = pack_bf16x2(p0, p1);
+                gs = add_bf16x2(pk[e], gs);
+            }
+            return gs;
+        };
+        // Weights of the two groups of sub-tile kt; if a lane's sum for
+        // either exceeds kGroupMax, the reference maximum moves to the
+        // maximum over both groups, O and the normaliser are rescaled and
+        // both groups' weights are formed again.
+        auto check = [&](int kt, uint32_t (&pa)[4], uint32_t (&pb)[4], float &ga, float &gb) {
+            if (__ballot(!(ga <= kGroupMax) || !(gb <= kGroupMax)) != 0ull) {
                 float mx = -INFINITY;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sacc[kt][8 * mm + e]);
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
                 const float mn = fmaxf(-nm, max_halves(mx) * scale2);
                 const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(-nm - mn);
                 nm = -mn;
@@ -415,15 +398,58 @@ __global__ __launch_bounds__(SINGLE ? BLK * 2 : BLK * 4, BLK == 128 ? 2 : 1) voi
                 for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-                weights(nm);
+                ga = weights(2 * kt, nm, pa);
+                gb = weights(2 * kt + 1, nm, pb);
             }
-            lsum += gsum;
+            lsum += ga + gb;
+        };
+        auto pv = [&](const uint32_t (&pk)[4], const uint4 (&v)[C::NDT]) {
             const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-            if (gi + 2 < 4) rdv(gi + 2, vf[gi + 2]);
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) o[dt] = mfma32x32x16(as_bf16x8(vf[gi][dt]), pb, o[dt]);
+            for (int dt = 0; dt < C::NDT; ++dt) o[dt] = mfma32x32x16(as_bf16x8(v[dt]), pb, o[dt]);
+        };
+
+#pragma unroll
+        for (int s = 0; s < LA; ++s) rd(s);
+#pragma unroll
+        for (int s = 0; s < C::NKS; ++s) {
+            rd(s + LA);
+            __builtin_amdgcn_sched_barrier(0);
+            sacc[0] = mfma32x32x16(as_bf16x8(kf[s]), qf[s], sacc[0]);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if (diag) mask_diag(0);
+
+        uint4 vf[4][C::NDT];
+        uint32_t pk[4][4];
+        float gs[4];
+        // Sub-tile 1's products, beside sub-tile 0's weights and the V^T
+        // fragments of groups 0 and 1.
+#pragma unroll
+        for (int s = C::NKS; s < NS; ++s) {
+            if (s + LA < NS) rd(s + LA);
+            sacc[1] = mfma32x32x16(as_bf16x8(kf[s]), qf[s - C::NKS], sacc[1]);
+        }
+        rdv(0, vf[0]);
+        rdv(1, vf[1]);
+        gs[0] = weights(0, nm, pk[0]);
+        gs[1] = weights(1, nm, pk[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        check(0, pk[0], pk[1], gs[0], gs[1]);
+        if (diag) mask_diag(1);
+
+        // Groups 0 and 1's products, beside sub-tile 1's weights and the V^T
+        // fragments of groups 2 and 3.
+        pv(pk[0], vf[0]);
+        pv(pk[1], vf[1]);
+        rdv(2, vf[2]);
+        rdv(3, vf[3]);
+        gs[2] = weights(2, nm, pk[2]);
+        gs[3] = weights(3, nm, pk[3]);
+        __builtin_amdgcn_sched_barrier(0);
+        check(1, pk[2], pk[3], gs[2], gs[3]);
+        pv(pk[2], vf[2]);
+        pv(pk[3], vf[3]);
     };
 
     // Stages are taken two at a time between barriers, from two pairs of
