@@ -14,7 +14,10 @@ the largest supported block count.
 * nb = 4096 (L = 524288 at B = 128), the largest list the selection takes:
   end to end, checked on sampled block-rows and tokens;
 * attention on rows of more than 512 blocks (head-pair work-groups) with an
-  odd G and with 64-row blocks, on random causal masks.
+  odd G and with 64-row blocks, on random causal masks;
+* attention on key logits that follow a random walk with large jumps up and
+  down, so the online softmax's reference maximum has to move at many key
+  positions and weights far below it underflow to zero.
 Rules as for the other parity tests: masks equal up to blocks within 1e-4 of
 the tau boundary, block scores to 1e-5 of the row total, attention outputs
 max |err| <= 1e-2 and mean <= 1e-3 (fp32 output).
@@ -232,6 +235,68 @@ def test_long_rows_head_pair_forms(case):
     toks = [(h, t) for h in range(Hq) for I in (0, 1, nb // 2, nb - 2, nb - 1)
             for t in range(I * B, min((I + 1) * B, L))]
     O_ref = oracle.attention(g["q"], g["k"], g["v"], B, mask, toks=toks)
+    O_np = O.cpu().numpy()
+    got = np.stack([O_np[t, h] for h, t in toks])
+    mx, mean = o_errors(got, O_ref)
+    print("  O on %d tokens: max %.3g mean %.3g" % (len(toks), mx, mean), flush=True)
+    assert mx <= O_MAX and mean <= O_MEAN
+
+
+# Key logits b_g[n] (natural units, the same for every query of kv-head g)
+# follow a random walk with +8 jumps and wrap at 120: the running maximum of a
+# row moves at many key positions (either 16-key group of a 32-key sub-tile,
+# either half of the lanes), and keys past a wrap fall up to 120 units below
+# it.  A span of 120 units (173 in log2) is more than fp32 can hold as
+# exp2(logit - m) for an m that stopped following the row maximum.
+JUMPS = [
+    # (L, Hq, Hkv, d, B)
+    (1216, 4, 2, 128, 128),           # one head per work-group, ragged last block
+    (640, 4, 4, 64, 64),              # 64-row blocks, G = 1
+    (520 * 128 - 37, 2, 1, 64, 128),  # rows of more than 512 blocks: head pairs
+]
+
+
+def _jump_inputs(L, Hq, Hkv, d, seed):
+    from tests.helpers import bf16
+    rng = np.random.default_rng(seed)
+    G = Hq // Hkv
+    u = rng.standard_normal((Hkv, d))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    steps = rng.normal(0.0, 0.3, size=(L, Hkv))
+    steps += 8.0 * (rng.uniform(size=(L, Hkv)) < 0.05)
+    b = np.mod(np.cumsum(steps, axis=0), 120.0)
+    k = b[:, :, None] * u[None, :, :] + 0.02 * rng.standard_normal((L, Hkv, d))
+    # q . k / sqrt(d) = b[n] for q = sqrt(d) u, plus a little per-head noise.
+    q = np.sqrt(d) * u[np.arange(Hq) // G][None, :, :] + 0.1 * rng.standard_normal((L, Hq, d))
+    v = rng.standard_normal((L, Hkv, d))
+    return bf16(q), bf16(k), bf16(v)
+
+
+@pytest.mark.parametrize("case", JUMPS, ids=[str(c) for c in JUMPS])
+def test_attention_on_jumping_logits(case):
+    rr = _rr()
+    L, Hq, Hkv, d, B = case
+    nb = (L + B - 1) // B
+    print("jumping logits %s nb=%d" % (case, nb), flush=True)
+    qb, kb, vb = _jump_inputs(L, Hq, Hkv, d, seed=41)
+    rng = np.random.default_rng(43)
+    mask = np.tril((rng.uniform(size=(Hq, nb, nb)) < 0.4).astype(np.uint8))
+    mask[:, np.arange(nb), np.arange(nb)] |= (rng.uniform(size=(Hq, nb)) < 0.5).astype(np.uint8)
+    for h in range(Hq):
+        for I in range(nb):
+            if not mask[h, I].any():
+                mask[h, I, rng.integers(0, I + 1)] = 1
+    counts, idx = oracle.list_from_mask(mask)
+    idx = np.where(np.arange(nb)[None, None, :] < counts[:, :, None], idx, -1).astype(np.int32)
+    O = rr.rr_sparse_attn(_dev(qb), _dev(kb), _dev(vb), B, torch.from_numpy(counts).cuda(),
+                          torch.from_numpy(idx).cuda(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    if nb > 512:
+        toks = [(h, t) for h in range(Hq) for I in (1, nb // 2, nb - 1)
+                for t in range(I * B, min((I + 1) * B, L))]
+    else:
+        toks = [(h, t) for h in range(Hq) for t in range(L)]
+    O_ref = oracle.attention(qb, kb, vb, B, mask, toks=toks)
     O_np = O.cpu().numpy()
     got = np.stack([O_np[t, h] for h, t in toks])
     mx, mean = o_errors(got, O_ref)
