@@ -282,15 +282,15 @@ __global__ __launch_bounds__(SINGLE ? BLK * 2 : BLK * 4, BLK == 128 ? 2 : 1) voi
 
     const int nst = nunion * C::SPB;
 
-    // Union entry of stage st: key block in the low 16 bits, bit 16+q set
-    // when head q of the pair keeps it.  Read from LDS, made wave-uniform.
-    auto stage_entry = [&](int st) -> int {
-        if (st >= nst) return -1;
-        return __builtin_amdgcn_readfirstlane((int)ulist[st / C::SPB]);
-    };
     // Copy target of stage st: a stage past the end re-copies the last one
     // (into a buffer no one reads), so every step issues the same copies.
     auto copy_stage = [&](int st) -> int { return min(st, nst - 1); };
+    // Union entry of the stage that step st copies: key block in the low 16
+    // bits, bit 16+q set when head q of the pair keeps it.  Read from LDS
+    // before the wait that precedes a barrier and made wave-uniform after
+    // it, so no LDS round trip follows the barrier.
+    auto raw_entry = [&](int st) -> uint32_t { return ulist[copy_stage(st) / C::SPB]; };
+    auto uni = [&](uint32_t r) -> int { return __builtin_amdgcn_readfirstlane((int)r); };
 
     // Per-lane byte offsets of this wave's copies inside one stage (the same
     // for every stage): K chunk (row r, slot c^swz) and V^T chunk.  Each copy
@@ -315,9 +315,8 @@ __global__ __launch_bounds__(SINGLE ? BLK * 2 : BLK * 4, BLK == 128 ? 2 : 1) voi
     // resource is based at the stage's first key row and ends after key row
     // L-1: the rows of a short last stage past L are read as zeros (their
     // scores are masked causally).  V^T is zero-padded to Lp.
-    auto issue = [&](int st, char *kb, char *vb) {
+    auto issue = [&](int st, int ent, char *kb, char *vb) {
         st = copy_stage(st);
-        const int ent = __builtin_amdgcn_readfirstlane((int)ulist[st / C::SPB]);
         const int J = ent & 0xffff;
         const int key0 = J * BLK + (st % C::SPB) * C::KT;
         const __amdgpu_buffer_rsrc_t rk =
@@ -456,56 +455,61 @@ __global__ __launch_bounds__(SINGLE ? BLK * 2 : BLK * 4, BLK == 128 ? 2 : 1) voi
     // buffers: while one pair is computed the copies of the next two stages
     // fill the other.  One barrier per pair: every wave's copies of the pair
     // have landed (vmcnt 0) and every wave has finished reading the other
-    // pair (lgkmcnt 0) before it.
+    // pair (lgkmcnt 0) before it.  The copies are issued between the pair's
+    // two stages rather than right after the barrier (measured faster: their
+    // landing then overlaps the second stage's products instead of the
+    // first's).
     if constexpr (SINGLE) {
         // One head: two buffers, one stage per barrier.
         if (nst > 0) {
-            issue(0, Kb0, Vb0);
+            issue(0, uni(raw_entry(0)), Kb0, Vb0);
             for (int st = 0; st < nst; st += 2) {
                 {
-                    const int E0 = stage_entry(st);
+                    const uint32_t r0 = raw_entry(st), r1 = raw_entry(st + 1);
                     wait_vmcnt<0>();
                     wait_lgkm0();
                     bar();
-                    issue(st + 1, Kb1, Vb1);
-                    compute(st, E0, Kb0, Vb0);
+                    issue(st + 1, uni(r1), Kb1, Vb1);
+                    compute(st, uni(r0), Kb0, Vb0);
                 }
                 if (st + 1 >= nst) break;
                 {
-                    const int E1 = stage_entry(st + 1);
+                    const uint32_t r1 = raw_entry(st + 1), r2 = raw_entry(st + 2);
                     wait_vmcnt<0>();
                     wait_lgkm0();
                     bar();
-                    issue(st + 2, Kb0, Vb0);
-                    compute(st + 1, E1, Kb1, Vb1);
+                    issue(st + 2, uni(r2), Kb0, Vb0);
+                    compute(st + 1, uni(r1), Kb1, Vb1);
                 }
             }
             wait_vmcnt<0>();
         }
     } else if (nst > 0) {
-        issue(0, Kb0, Vb0);
-        issue(1, Kb1, Vb1);
+        issue(0, uni(raw_entry(0)), Kb0, Vb0);
+        issue(1, uni(raw_entry(1)), Kb1, Vb1);
         for (int st = 0; st < nst; st += 4) {
             {
-                const int E0 = stage_entry(st), E1 = stage_entry(st + 1);
+                const uint32_t r0 = raw_entry(st), r1 = raw_entry(st + 1);
+                const uint32_t r2 = raw_entry(st + 2), r3 = raw_entry(st + 3);
                 wait_vmcnt<0>();
                 wait_lgkm0();
                 bar();
-                issue(st + 2, Kb2, Vb2);
-                issue(st + 3, Kb3, Vb3);
-                compute(st, E0, Kb0, Vb0);
-                compute(st + 1, E1, Kb1, Vb1);
+                compute(st, uni(r0), Kb0, Vb0);
+                issue(st + 2, uni(r2), Kb2, Vb2);
+                issue(st + 3, uni(r3), Kb3, Vb3);
+                compute(st + 1, st + 1 < nst ? uni(r1) : -1, Kb1, Vb1);
             }
             if (st + 2 >= nst) break;
             {
-                const int E2 = stage_entry(st + 2), E3 = stage_entry(st + 3);
+                const uint32_t r2 = raw_entry(st + 2), r3 = raw_entry(st + 3);
+                const uint32_t r4 = raw_entry(st + 4), r5 = raw_entry(st + 5);
                 wait_vmcnt<0>();
                 wait_lgkm0();
                 bar();
-                issue(st + 4, Kb0, Vb0);
-                issue(st + 5, Kb1, Vb1);
-                compute(st + 2, E2, Kb2, Vb2);
-                compute(st + 3, E3, Kb3, Vb3);
+                compute(st + 2, uni(r2), Kb2, Vb2);
+                issue(st + 4, uni(r4), Kb0, Vb0);
+                issue(st + 5, uni(r5), Kb1, Vb1);
+                compute(st + 3, st + 3 < nst ? uni(r3) : -1, Kb3, Vb3);
             }
         }
         wait_vmcnt<0>();
