@@ -15,8 +15,9 @@
 //   * the K tiles [64 keys][d] and V^T tiles [d][64 keys] of the next two
 //     stages are copied global -> LDS by buffer_load_dwordx4 ... lds (no
 //     registers) into one pair of buffers while the two stages held by the
-//     other pair are computed, with one barrier per pair of stages; rows are
-//     XOR-swizzled in 16-byte slots against LDS bank conflicts;
+//     other pair are computed, with one barrier per pair of stages and the
+//     copies issued between the pair's two stages; rows are XOR-swizzled in
+//     16-byte slots against LDS bank conflicts;
 //   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16.  The K rows fed to the
 //     matrix unit are permuted so that accumulator register e of lane
 //     (column q, half hk) holds key 16*hk + e of each 32-key sub-tile:
@@ -24,8 +25,8 @@
 //     taken, needs a single cross-half exchange;
 //   * online softmax in the log2 domain (scores pre-scaled by
 //     log2(e)/sqrt(d)), diagonal block masked causally; the running maximum
-//     is checked through each 16-key group's weight sum rather than taken
-//     per score;
+//     is checked through the weight sums of each 32-key sub-tile's two
+//     16-key groups rather than taken per score;
 //   * P^T is rounded to bf16 in registers and used directly as the B operand
 //     of O^T += V^T . P^T: its registers already hold 8 consecutive keys per
 //     lane half, and the matching V^T rows are 16-byte LDS reads.
@@ -41,15 +42,16 @@
 // the 8 XCDs by block index; a fixed mapping from block index to rows left
 // the XCDs with up to 41% different work on the 64K video shape.)
 //
-// Up to 512 blocks (SINGLE) a work-group serves one query head: BLK/32 waves,
-// two stage buffers with one barrier per stage, and LDS for two work-groups
-// per CU.  The work-groups are persistent (two per CU, looping over items),
+// For rows of up to 128 blocks, and of up to 512 blocks when G is odd (the
+// last head pair would hold a single head), a work-group serves one query
+// head (SINGLE): BLK/32 waves, two stage buffers with one barrier per stage,
+// and LDS for two work-groups per CU.  The work-groups are persistent (two per CU, looping over items),
 // and the two waves a SIMD holds then belong to different work-groups whose
 // barriers are independent, so one wave's softmax meets the other's
 // products more often than in the head-pair work-group, whose barrier keeps
 // its two waves per SIMD in step; no wave waits on a stage its head did not
-// keep.  Longer rows keep the head pairs: there, sharing each staged K/V tile
-// between two heads matters more.
+// keep.  Otherwise head pairs serve: on longer rows sharing each staged K/V
+// tile between two heads matters more.
 #include <algorithm>
 
 #include "rr_device.h"
@@ -549,6 +551,8 @@ hipError_t launch_transpose_v(const uint16_t *V, const Shape &s, uint16_t *Vt, u
 
 // Longest block count for which the persistent form is launched.
 constexpr int kPersistMaxNb = 512;
+// Longest block count for which one head per work-group serves every G.
+constexpr int kSingleMaxNb = 128;
 // Items per resident work-group (one per CU with head pairs, two with one
 // head) up to which the items of all kv-heads are interleaved (block-rows
 // descending over every kv-head: the longest rows start first, which matters
@@ -608,9 +612,14 @@ static void launch_fa_t(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt
 hipError_t launch_block_sparse_fa(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt,
                                   unsigned *counter, const Shape &s, const int32_t *counts,
                                   const int32_t *block_idx, void *O, bool out_f32, hipStream_t st) {
-    // Up to kPersistMaxNb blocks: one query head per work-group, two
-    // work-groups per CU (the persistent form); longer rows: head pairs.
-    const bool single = s.nb <= kPersistMaxNb;
+    // One query head per work-group, two work-groups per CU (the persistent
+    // form), for short rows, and up to kPersistMaxNb blocks for an odd G,
+    // whose last head pair would hold a single head; head pairs otherwise.
+    // Measured against the other form: 8K Llama-shaped rows (64 blocks)
+    // 2.5% faster with one head, 32K (256 blocks, G = 4) 3.5% faster in
+    // pairs, the 64K video shape (512 blocks, G = 7) 11% faster with one
+    // head.
+    const bool single = s.nb <= kSingleMaxNb || ((s.Hq / s.Hkv) % 2 == 1 && s.nb <= kPersistMaxNb);
     if (s.d == 128 && s.B == 128) {
         if (single) launch_fa_t<128, 128, true>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
         else launch_fa_t<128, 128, false>(Q, K, Vt, counter, s, counts, block_idx, O, out_f32, st);
