@@ -151,7 +151,11 @@ int rr_select(const float *block_scores, int Hq, int L, int B, float tau, int32_
  * For token t in block I = t / B and head h the keys are the n <= t whose
  * block n / B is listed in block_idx[h][I][0 .. counts[h][I]); softmax of
  * (1/sqrt(d)) Q[t][h] . K[n][g] over them, applied to V[n][g].
- * Lists must be ascending, in range J <= I, and non-empty.
+ * Lists are read as rr_select writes them: ascending, in range J <= I.  Any
+ * other list is accepted too: an entry out of range or repeated is ignored,
+ * and the listed blocks are taken in ascending order whatever their order in
+ * the list (the output is then bitwise that of the sorted list).  A row whose
+ * list holds no valid block gets O = 0.
  *   O         out, [L][Hq][d] in o_dtype (rr_out_dtype).
  *   ws        device workspace, >= rr_sparse_attn_workspace_bytes(...).
  */

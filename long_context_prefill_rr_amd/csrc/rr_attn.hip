@@ -187,10 +187,13 @@ __global__ __launch_bounds__(SINGLE ? BLK * 2 : BLK * 4, BLK == 128 ? 2 : 1) voi
     // descending, then kv-head, then head pair, so the longest rows of every
     // kv-head of a chunk start first.  Every wave of the work-group
     // reads the same item, so all leave together.
-    __shared__ int item_sh;
+    __shared__ int item_sh, bad_sh;
     for (;;) {
     __syncthreads();   // every wave is done with the previous item's LDS
-    if (tid == 0) item_sh = (int)atomicAdd(counter, 1u);
+    if (tid == 0) {
+        item_sh = (int)atomicAdd(counter, 1u);
+        bad_sh = 0;
+    }
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(item_sh);
     if (item >= nitems) break;
@@ -206,11 +209,29 @@ __global__ __launch_bounds__(SINGLE ? BLK * 2 : BLK * 4, BLK == 128 ? 2 : 1) voi
     const int tq = I * BLK + rw * 32 + col;
     const int wave_last_row = I * BLK + rw * 32 + 31;
 
+    // With SINGLE, a strictly ascending list of blocks J <= I (what the
+    // selection writes) is copied into LDS as it is; any other list, and the
+    // two lists of a head pair, take the general path below.
+    bool listed = false;
+    if constexpr (SINGLE) {
+        const int cq = min(max(counts[(size_t)h * nb + I], 0), nb);
+        const int32_t *lq = block_idx + ((size_t)h * nb + I) * nb;
+        for (int k = tid; k < cq; k += C::NT) {
+            const int J = lq[k];
+            const int Jn = k + 1 < cq ? lq[k + 1] : I + 1;
+            if (!(J >= 0 && J < Jn)) bad_sh = 1;
+            ulist[k] = (uint32_t)J | (1u << 16);
+        }
+        if (tid == 0) nunion = cq;
+        __syncthreads();
+        listed = bad_sh == 0;
+    }
     // Union of the two heads' kept lists (ascending key blocks, each tagged
     // with the heads that keep it; with SINGLE the one head's list), built in
     // LDS: membership bitmaps, then a work-group scan compacts the set blocks
     // in index order.  The bitmaps also drop repeated and out-of-range
     // entries of a malformed list.
+    if (!listed) {
     for (int i = tid; i < 2 * (C::MAXNB / 32); i += C::NT) (&bits[0][0])[i] = 0u;
     __syncthreads();
 #pragma unroll
@@ -253,6 +274,7 @@ __global__ __launch_bounds__(SINGLE ? BLK * 2 : BLK * 4, BLK == 128 ? 2 : 1) voi
         if (tid == C::NT - 1) nunion = pre + incl;
         __syncthreads();
     }
+    }  // general path
 
     bf16x8 qf[C::NKS];
     {

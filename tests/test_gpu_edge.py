@@ -302,3 +302,56 @@ def test_attention_on_jumping_logits(case):
     mx, mean = o_errors(got, O_ref)
     print("  O on %d tokens: max %.3g mean %.3g" % (len(toks), mx, mean), flush=True)
     assert mx <= O_MAX and mean <= O_MEAN
+
+
+# Kept lists as rr_select writes them are strictly ascending; one head per
+# work-group copies such a list into LDS as it is, and merges any other list
+# (unordered, repeated or out-of-range entries) through its membership
+# bitmaps.  Both must walk the same blocks in the same order, so the outputs
+# are bitwise equal.
+UNSORTED = [
+    # (L, Hq, Hkv, d, B)
+    (1216, 8, 2, 128, 128),   # G = 4, ragged last block
+    (2048, 7, 1, 128, 128),   # G = 7
+    (1024, 4, 4, 64, 128),    # G = 1, d = 64
+]
+
+
+@pytest.mark.parametrize("case", UNSORTED, ids=[str(c) for c in UNSORTED])
+def test_attention_on_unsorted_lists(case):
+    rr = _rr()
+    L, Hq, Hkv, d, B = case
+    w, g = small_workload(kind="llama", L=L, Hq=Hq, Hkv=Hkv, d=d, B=B, S=8, seed=47)
+    nb = w.nb
+    print("unsorted lists %s nb=%d" % (case, nb), flush=True)
+    rng = np.random.default_rng(53)
+    mask = np.tril((rng.uniform(size=(Hq, nb, nb)) < 0.5).astype(np.uint8))
+    for h in range(Hq):
+        for I in range(nb):
+            if not mask[h, I].any():
+                mask[h, I, rng.integers(0, I + 1)] = 1
+    counts, idx = oracle.list_from_mask(mask)
+    idx = np.where(np.arange(nb)[None, None, :] < counts[:, :, None], idx, -1).astype(np.int32)
+    # Shuffle every row; where a row has room, repeat one entry and add one
+    # past the diagonal (both must be dropped).
+    counts2, idx2 = counts.copy(), idx.copy()
+    for h in range(Hq):
+        for I in range(nb):
+            c = int(counts[h, I])
+            row = list(idx[h, I, :c])
+            rng.shuffle(row)
+            if c + 2 <= nb:
+                row = row + [row[0], I + 1 if I + 1 < nb else -1]
+            idx2[h, I, :len(row)] = row
+            counts2[h, I] = len(row)
+    q, k, v = _dev(g["q"]), _dev(g["k"]), _dev(g["v"])
+    O1 = rr.rr_sparse_attn(q, k, v, B, torch.from_numpy(counts).cuda(), torch.from_numpy(idx).cuda(),
+                           out_dtype=torch.float32)
+    O2 = rr.rr_sparse_attn(q, k, v, B, torch.from_numpy(counts2).cuda(), torch.from_numpy(idx2).cuda(),
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2)
+    O_ref = oracle.attention(g["q"], g["k"], g["v"], B, mask)
+    mx, mean = o_errors(O1.cpu().numpy(), O_ref)
+    print("  O: max %.3g mean %.3g" % (mx, mean), flush=True)
+    assert mx <= O_MAX and mean <= O_MEAN
