@@ -164,8 +164,8 @@ def cpu_baseline(w, g, dense_flops, att_rows, tokens_per_row=16):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload index 0..4")
     ap.add_argument("--S", type=int, default=None)
     ap.add_argument("--tau", type=float, default=None)
