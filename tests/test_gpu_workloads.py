@@ -11,6 +11,9 @@ benchmark times (bf16 inputs, one layer, the default stream).
   heads and block-rows (the first and the last block-row included).  Bar:
   max |err| <= 1e-2, mean |err| <= 1e-3.  rr_prefill's own output under its
   own mask is held to the same bar on the same tokens.
+* The benchmark's own call (rr_prefill with bf16 output): its kept lists
+  equal the fp32 call's and its output equals the fp32 output rounded to
+  bf16, bit for bit, on every element.
 Each case prints one JSON line with its counts and errors.
 """
 import json
@@ -82,6 +85,15 @@ def test_workload_parity(cfg, S, tau):
     nb = w.nb
 
     O, counts, idx = rr.rr_prefill(q, k, v, w.B, w.S, w.tau, out_dtype=torch.float32)
+    # The benchmark's configuration: the same call with bf16 output.  The
+    # kept lists must repeat exactly, and O must be the fp32 output rounded
+    # to bf16 (round to nearest even): the two kernels differ only in the
+    # final store.
+    Ob, counts_b, idx_b = rr.rr_prefill(q, k, v, w.B, w.S, w.tau, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    bf16_lists_equal = bool(torch.equal(counts_b, counts) and torch.equal(idx_b, idx))
+    bf16_out_equal = bool(torch.equal(Ob, O.to(torch.bfloat16)))
+    del Ob, counts_b, idx_b
     A_gpu = rr.rr_estimate(q, k, w.B, w.S)
     torch.cuda.synchronize()
     counts_np, idx_np = counts.cpu().numpy(), idx.cpu().numpy()
@@ -132,9 +144,11 @@ def test_workload_parity(cfg, S, tau):
                mask=dict((k_, v_) for k_, v_ in res.items() if k_ != "examples"),
                mask_examples=res["examples"], block_score_err=a_err,
                o_block_rows_checked=n_rows_o, o_tokens_checked=n_tok,
-               o_max_err=o_max, o_mean_err=o_mean, e2e_o_max_err=e2e_max, e2e_o_mean_err=e2e_mean)
+               o_max_err=o_max, o_mean_err=o_mean, e2e_o_max_err=e2e_max, e2e_o_mean_err=e2e_mean,
+               bf16_call_lists_equal=bf16_lists_equal, bf16_call_out_equal_rounded_f32=bf16_out_equal)
     print("PARITY " + json.dumps(out), flush=True)
     assert a_err <= BLOCK_SCORE_TOL
     assert res["unexcused"] == 0
     assert o_max <= O_MAX and o_mean <= O_MEAN
     assert e2e_max <= O_MAX and e2e_mean <= O_MEAN
+    assert bf16_lists_equal and bf16_out_equal
